@@ -1,0 +1,327 @@
+// Row-wise kernels of the MLA path: cache-row epilogue of the KV compression, the query
+// RMSNorm and packing, index preparation, the split-K merge and the prefill gather.
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla {
+
+// ------------------------------------------------------------------ compress epilogue
+// One block per token.  a = sum of the kv_a partials = [latent (dc) | k_pe (dr)].
+// latent <- latent / sqrt(mean(latent^2) + eps) * gamma;  k_pe <- RoPE(k_pe, pos);
+// the row is rounded to the cache format and written to its slot (skipped if out of range).
+template <typename ActT, int CACHE>
+__global__ __launch_bounds__(256) void compress_rows_kernel(
+    int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
+    const int32_t* __restrict__ pos, const int64_t* __restrict__ slots, void* __restrict__ cache,
+    float* __restrict__ cache_scale, long num_slots, float eps, float theta) {
+  extern __shared__ float row[];                    // [dc + dr]
+  __shared__ float red[16];
+  const int t = blockIdx.x, W = dc + dr;
+  const long slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;        // uniform over the block
+  for (int i = threadIdx.x; i < W; i += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += acc[(long(s) * T + t) * W + i];
+    row[i] = v;
+  }
+  __syncthreads();
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < dc; i += blockDim.x) ss += row[i] * row[i];
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / float(dc) + eps);
+  for (int i = threadIdx.x; i < dc; i += blockDim.x) row[i] = row[i] * r * ldf<ActT>(gamma, i);
+  const int p = pos[t];
+  for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) {
+    float c, s;
+    rope_cs(p, i, dr, theta, &c, &s);
+    float e = row[dc + 2 * i], o = row[dc + 2 * i + 1];
+    row[dc + 2 * i] = e * c - o * s;
+    row[dc + 2 * i + 1] = e * s + o * c;
+  }
+  __syncthreads();
+  if (CACHE == K_F32) {
+    float* dst = static_cast<float*>(cache) + slot * W;
+    for (int i = threadIdx.x; i < W; i += blockDim.x) dst[i] = row[i];
+  } else if (CACHE == K_BF16) {
+    uint16_t* dst = static_cast<uint16_t*>(cache) + slot * W;
+    for (int i = threadIdx.x; i < W; i += blockDim.x) dst[i] = f2bf(row[i]);
+  } else {
+    float am = 0.f;
+    for (int i = threadIdx.x; i < W; i += blockDim.x) am = fmaxf(am, fabsf(row[i]));
+    am = block_max(am, red);
+    const float sc = am > 0.f ? __fdiv_rn(am, 448.0f) : 1.0f;
+    uint8_t* dst = static_cast<uint8_t*>(cache) + slot * W;
+    for (int i = threadIdx.x; i < W; i += blockDim.x) dst[i] = uint8_t(f_to_e4m3(__fdiv_rn(row[i], sc)));
+    if (threadIdx.x == 0) cache_scale[slot] = sc;
+  }
+}
+
+void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit, const float* acc,
+                          const void* gamma, const int32_t* pos, const int64_t* slots,
+                          void* cache_data, float* cache_scale, long num_slots, float eps,
+                          float theta, hipStream_t st) {
+  if (T <= 0) return;
+  size_t sh = size_t(dc + dr) * sizeof(float);
+#define MLA_CR(A, C)                                                                          \
+  hipLaunchKernelGGL((compress_rows_kernel<A, C>), dim3(T), dim3(256), sh, st, dc, dr, T, nsplit, \
+                     acc, static_cast<const A*>(gamma), pos, slots, cache_data, cache_scale,      \
+                     num_slots, eps, theta)
+  if (act == K_F32) {
+    MLA_CR(float, K_F32);
+  } else if (cache == K_BF16) {
+    MLA_CR(uint16_t, K_BF16);
+  } else {
+    MLA_CR(uint16_t, K_FP8);
+  }
+#undef MLA_CR
+}
+
+// ------------------------------------------------------------------ RMSNorm of query latents
+template <typename ActT>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsplit,
+                                                           const float* __restrict__ acc,
+                                                           const ActT* __restrict__ gamma,
+                                                           ActT* __restrict__ out, float eps) {
+  extern __shared__ float row[];
+  __shared__ float red[16];
+  const int t = blockIdx.x;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += acc[(long(s) * T + t) * n + i];
+    row[i] = v;
+    ss += v * v;
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / float(n) + eps);
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    stf<ActT>(out, long(t) * n + i, row[i] * r * ldf<ActT>(gamma, i));
+}
+
+void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,
+                         void* out, float eps, hipStream_t st) {
+  if (T <= 0) return;
+  size_t sh = size_t(n) * sizeof(float);
+  if (act == K_F32)
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<float>, dim3(T), dim3(256), sh, st, T, n, nsplit, acc,
+                       static_cast<const float*>(gamma), static_cast<float*>(out), eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<uint16_t>, dim3(T), dim3(256), sh, st, T, n, nsplit, acc,
+                       static_cast<const uint16_t*>(gamma), static_cast<uint16_t*>(out), eps);
+}
+
+// ------------------------------------------------------------------ query packing
+// Block per token; thread loop over heads x (nope values + rope pairs).  ACT is the absorbed
+// outputs' storage, QS the explicit output's.
+template <int ACT, int QS>
+__global__ __launch_bounds__(256) void q_pack_kernel(bool absorbed, int T, int H, int dn, int dr, int dc,
+                                                     int nsplit, const float* __restrict__ q_acc,
+                                                     const int32_t* __restrict__ pos, float scale, float theta,
+                                                     typename StoreT<ACT>::type* __restrict__ qnope,
+                                                     typename StoreT<ACT>::type* __restrict__ qhat,
+                                                     typename StoreT<QS>::type* __restrict__ qs) {
+  const int t = blockIdx.x;
+  const int dqk = dn + dr, half = dr / 2;
+  const long nq = long(H) * dqk;
+  const int per_head = dn + half;
+  const int p = pos[t];
+  auto q_at = [&](long j) -> float {
+    float v = 0.f;
+    for (int s = 0; s < nsplit; ++s) v += q_acc[(long(s) * T + t) * nq + j];
+    return v;
+  };
+  for (int e = threadIdx.x; e < H * per_head; e += blockDim.x) {
+    const int h = e / per_head, i = e % per_head;
+    const long base = long(h) * dqk;
+    if (i < dn) {
+      float v = scale * q_at(base + i);
+      if (absorbed) sts_<ACT>(qnope, (long(t) * H + h) * dn + i, v);
+      else sts_<QS>(qs, (long(t) * H + h) * dqk + i, v);
+    } else {
+      const int pi = i - dn;
+      float c, s;
+      rope_cs(p, pi, dr, theta, &c, &s);
+      float ev = q_at(base + dn + 2 * pi), ov = q_at(base + dn + 2 * pi + 1);
+      float re = scale * (ev * c - ov * s), ro = scale * (ev * s + ov * c);
+      if (absorbed) {
+        long o = (long(t) * H + h) * (dc + dr) + dc + 2 * pi;
+        sts_<ACT>(qhat, o, re);
+        sts_<ACT>(qhat, o + 1, ro);
+      } else {
+        long o = (long(t) * H + h) * dqk + dn + 2 * pi;
+        sts_<QS>(qs, o, re);
+        sts_<QS>(qs, o + 1, ro);
+      }
+    }
+  }
+}
+
+void launch_q_pack(int act, int qs_type, bool absorbed, int T, int H, int dn, int dr, int dc, int nsplit,
+                   const float* q_acc, const int32_t* pos, float scale, float theta, void* qnope, void* qhat,
+                   void* qs, hipStream_t st) {
+  if (T <= 0) return;
+  if (act == K_F32)
+    hipLaunchKernelGGL((q_pack_kernel<S_F32, S_F32>), dim3(T), dim3(256), 0, st, absorbed, T, H, dn, dr, dc,
+                       nsplit, q_acc, pos, scale, theta, static_cast<float*>(qnope), static_cast<float*>(qhat),
+                       static_cast<float*>(qs));
+  else if (qs_type == K_F16)
+    hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_F16>), dim3(T), dim3(256), 0, st, absorbed, T, H, dn, dr, dc,
+                       nsplit, q_acc, pos, scale, theta, static_cast<uint16_t*>(qnope),
+                       static_cast<uint16_t*>(qhat), static_cast<uint16_t*>(qs));
+  else
+    hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_BF16>), dim3(T), dim3(256), 0, st, absorbed, T, H, dn, dr, dc,
+                       nsplit, q_acc, pos, scale, theta, static_cast<uint16_t*>(qnope),
+                       static_cast<uint16_t*>(qhat), static_cast<uint16_t*>(qs));
+}
+
+// In-place RoPE of the q_pe part of fp16 queries (the projection already wrote them scaled).
+__global__ __launch_bounds__(256) void q_rope_f16_kernel(int H, int dn, int dr, const int32_t* __restrict__ pos,
+                                                         float theta, uint16_t* __restrict__ qs) {
+  const int t = blockIdx.x, half = dr / 2, dqk = dn + dr;
+  const int p = pos[t];
+  for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
+    const int h = e / half, pi = e % half;
+    float c, s;
+    rope_cs(p, pi, dr, theta, &c, &s);
+    uint16_t* q = qs + (long(t) * H + h) * dqk + dn + 2 * pi;
+    float ev = h2f(q[0]), ov = h2f(q[1]);
+    q[0] = f2h(ev * c - ov * s);
+    q[1] = f2h(ev * s + ov * c);
+  }
+}
+
+void launch_q_rope_f16(int T, int H, int dn, int dr, const int32_t* pos, float theta, void* qs, hipStream_t st) {
+  if (T <= 0) return;
+  hipLaunchKernelGGL(q_rope_f16_kernel, dim3(T), dim3(256), 0, st, H, dn, dr, pos, theta, static_cast<uint16_t*>(qs));
+}
+
+// ------------------------------------------------------------------ positions and slots
+__global__ void decode_prep_kernel(int B, const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt,
+                                   int max_blocks, int32_t* __restrict__ pos, int64_t* __restrict__ slot) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int p = ctx[b] - 1;
+  int page = p >= 0 ? p / kPage : -1;
+  pos[b] = p > 0 ? p : 0;
+  slot[b] = (page >= 0 && page < max_blocks) ? int64_t(bt[long(b) * max_blocks + page]) * kPage + p % kPage : -1;
+}
+
+void launch_decode_prep(int B, const int32_t* ctx, const int32_t* bt, int max_blocks, int32_t* pos,
+                        int64_t* slot, hipStream_t st) {
+  hipLaunchKernelGGL(decode_prep_kernel, dim3((B + 255) / 256), dim3(256), 0, st, B, ctx, bt, max_blocks,
+                     pos, slot);
+}
+
+__global__ void prefill_prep_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
+                                    const int32_t* __restrict__ bt, int max_blocks,
+                                    int32_t* __restrict__ pos, int64_t* __restrict__ slot) {
+  const int s = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = cu[s] + i;
+  if (t >= cu[s + 1]) return;
+  const int p = start[s] + i;
+  const int page = p / kPage;
+  pos[t] = p;
+  slot[t] = (p >= 0 && page < max_blocks) ? int64_t(bt[long(s) * max_blocks + page]) * kPage + p % kPage : -1;
+}
+
+void launch_prefill_prep(int S, int max_q, const int32_t* cu, const int32_t* start, const int32_t* bt,
+                         int max_blocks, int32_t* pos, int64_t* slot, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3((max_q + 255) / 256, S), dim3(256), 0, st, cu, start, bt,
+                     max_blocks, pos, slot);
+}
+
+// ------------------------------------------------------------------ split-K merge
+// For each (b, h): m = max_j m_j, w_j = 2^(m_j - m), otilde = sum_j w_j o_j / sum_j w_j l_j.
+// Partial states use base-2 exponents (scores carry a log2 e factor).  Empty splits have
+// m_j = -inf and l_j = 0 and weigh nothing.
+template <bool HILO>
+__global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int splits,
+                                                           const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           void* __restrict__ otilde) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, part_ml[((long(b) * splits + s) * H + h) * 2]);
+  float l = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* ml = part_ml + ((long(b) * splits + s) * H + h) * 2;
+    if (ml[0] != -INFINITY) l += exp2f(ml[0] - m) * ml[1];
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  for (int c = threadIdx.x; c < dc; c += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const long base = (long(b) * splits + s) * H + h;
+      float ms = part_ml[base * 2];
+      if (ms != -INFINITY) v += exp2f(ms - m) * part_o[base * dc + c];
+    }
+    v *= inv;
+    if (HILO) {
+      uint16_t* o = static_cast<uint16_t*>(otilde) + (long(b) * H + h) * 2 * dc;
+      const uint16_t hi = f2bf(v);
+      o[c] = hi;
+      o[dc + c] = f2bf(v - bf2f(hi));
+    } else {
+      static_cast<float*>(otilde)[(long(b) * H + h) * dc + c] = v;
+    }
+  }
+}
+
+void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
+                         const float* part_ml, void* otilde, hipStream_t st) {
+  if (act == K_F32)
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(H, B), dim3(256), 0, st, H, dc, splits, part_o, part_ml,
+                       otilde);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(H, B), dim3(256), 0, st, H, dc, splits, part_o, part_ml,
+                       otilde);
+}
+
+// ------------------------------------------------------------------ prefill gather
+// lat[s][t][:] = dequantised cache row of position t of sequence s, t < ctx_s; zero beyond.
+template <typename ActT, int CACHE>
+__global__ __launch_bounds__(256) void gather_rows_kernel(int max_ctx, int W, const int32_t* __restrict__ cu,
+                                                          const int32_t* __restrict__ start,
+                                                          const int32_t* __restrict__ bt, int max_blocks,
+                                                          const void* __restrict__ cache,
+                                                          const float* __restrict__ cache_scale,
+                                                          ActT* __restrict__ lat) {
+  const int s = blockIdx.y, t = blockIdx.x;
+  const int ctx = start[s] + (cu[s + 1] - cu[s]);
+  ActT* dst = lat + (long(s) * max_ctx + t) * W;
+  if (t >= ctx) {
+    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, 0.f);
+    return;
+  }
+  const long slot = long(bt[long(s) * max_blocks + t / kPage]) * kPage + t % kPage;
+  if (CACHE == K_F32) {
+    const float* src = static_cast<const float*>(cache) + slot * W;
+    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, src[i]);
+  } else if (CACHE == K_BF16) {
+    const uint16_t* src = static_cast<const uint16_t*>(cache) + slot * W;
+    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, bf2f(src[i]));
+  } else {
+    const uint8_t* src = static_cast<const uint8_t*>(cache) + slot * W;
+    const float sc = cache_scale[slot];
+    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, sc * e4m3_to_f(src[i]));
+  }
+}
+
+void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, const int32_t* cu,
+                        const int32_t* start, const int32_t* bt, int max_blocks, const void* cache_data,
+                        const float* cache_scale, void* lat, hipStream_t st) {
+  dim3 grid(max_ctx, S);
+#define MLA_GR(A, C)                                                                             \
+  hipLaunchKernelGGL((gather_rows_kernel<A, C>), grid, dim3(256), 0, st, max_ctx, W, cu, start, bt, \
+                     max_blocks, cache_data, cache_scale, static_cast<A*>(lat))
+  if (act == K_F32) {
+    MLA_GR(float, K_F32);
+  } else if (cache == K_BF16) {
+    MLA_GR(uint16_t, K_BF16);
+  } else {
+    MLA_GR(uint16_t, K_FP8);
+  }
+#undef MLA_GR
+}
+
+}  // namespace mla

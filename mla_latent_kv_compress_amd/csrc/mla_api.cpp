@@ -1,0 +1,262 @@
+// extern "C" entry points of libmla: validate on the host, then enqueue the kernel pipeline.
+#include <hip/hip_runtime.h>
+
+#include "mla.h"
+#include "mla_kernels.h"
+#include "mla_plan.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+int kdt(int dt) { return dt == MLA_F32 ? K_F32 : dt == MLA_BF16 ? K_BF16 : K_FP8; }
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+int finish() { return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Y = X * W^T (TN) or X * W (NN), fp32 or bf16 inputs per the path; `out` is the bf16 path's
+// output storage (K_F32 / K_BF16 / K_F16; the fp32 path always writes fp32).
+GemmArgs gemm(Path path, bool nn, int out, int M, int N, int K, SplitK sk, int batch, const void* X,
+              long lda, long sx, const void* W, long ldw, long sw, void* Y, long ldc, long sy,
+              float alpha = 1.f, int kwrap = 0) {
+  GemmArgs g;
+  g.kind = path == PATH_F32 ? GEMM_F32 : GEMM_BF16;
+  g.nn = nn;
+  g.out = path == PATH_F32 ? K_F32 : out;
+  g.kwrap = kwrap;
+  g.M = M; g.N = N; g.K = K;
+  g.kchunk = sk.chunk; g.nsplit = sk.n; g.batch = batch;
+  g.X = X; g.lda = lda; g.sx = sx;
+  g.W = W; g.ldw = ldw; g.sw = sw;
+  g.Y = Y; g.ldc = ldc; g.sy = sy; g.ssplit = long(M) * ldc;
+  g.alpha = alpha;
+  return g;
+}
+
+SplitK whole(int K) { return SplitK{1, (K + 31) / 32 * 32}; }
+
+// kv_a projection of T tokens into fp32 partials, then the row epilogue into the cache.
+void enqueue_compress(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
+                      const void* hidden, const int32_t* pos, const int64_t* slots,
+                      const mla_cache* cache, int T, const CompressPlan& cp, void* ws,
+                      hipStream_t s) {
+  float* acc = reinterpret_cast<float*>(at(ws, cp.off_acc));
+  launch_gemm(gemm(path, false, K_F32, T, d.W(), d.D, cp.split, 1, hidden, d.D, 0, w->kv_a_proj, d.D, 0,
+                   acc, d.W(), 0), s);
+  launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), T, d.dc, d.dr, cp.split.n, acc,
+                       w->kv_a_norm, pos, slots, cache->data, cache->scale,
+                       long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.theta, s);
+}
+
+// Query projection of T tokens.  Leaves fp32 partials at q.off_q_acc, or (q.direct) the scaled
+// fp16 queries in `direct_out` ([T][H][dqk]).
+void enqueue_query(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
+                   const void* hidden, int T, const QueryPlan& q, void* ws, void* direct_out,
+                   float direct_scale, hipStream_t s) {
+  const long nq = long(d.H) * d.dqk();
+  void* qout = q.direct ? direct_out : at(ws, q.off_q_acc);
+  const int out = q.direct ? K_F16 : K_F32;
+  const float alpha = q.direct ? direct_scale : 1.f;
+  const void* x = hidden;
+  long ldx = d.D;
+  if (d.dq > 0) {
+    float* qa = reinterpret_cast<float*>(at(ws, q.off_qa_acc));
+    void* cq = at(ws, q.off_cq);
+    launch_gemm(gemm(path, false, K_F32, T, d.dq, d.D, q.split_a, 1, hidden, d.D, 0, w->q_a_proj, d.D, 0,
+                     qa, d.dq, 0), s);
+    launch_rmsnorm_rows(kdt(cfg->act_dtype), T, d.dq, q.split_a.n, qa, w->q_a_norm, cq, d.eps, s);
+    x = cq;
+    ldx = d.dq;
+  }
+  launch_gemm(gemm(path, false, out, T, int(nq), int(ldx), q.split_b, 1, x, ldx, 0, w->q_b_proj, ldx, 0, qout,
+                   nq, 0, alpha), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t mla_compress_append_workspace_size(const mla_config* cfg, int32_t num_tokens) {
+  Dims d;
+  Path path;
+  if (check_config(cfg, &d, &path) != MLA_OK || num_tokens < 0) return 0;
+  Layout L;
+  CompressPlan cp;
+  plan_compress(d, path, num_tokens, L, &cp);
+  return L.top;
+}
+
+int mla_compress_append(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                        const int32_t* positions, const int64_t* slot_mapping, const mla_cache* cache,
+                        int32_t num_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_compress_args(cfg, w, hidden, positions, slot_mapping, cache, num_tokens);
+  if (st != MLA_OK) return st;
+  Dims d;
+  Path path;
+  check_config(cfg, &d, &path);
+  if (num_tokens == 0) return MLA_OK;
+  Layout L;
+  CompressPlan cp;
+  plan_compress(d, path, num_tokens, L, &cp);
+  if (!workspace || workspace_bytes < L.top) return MLA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  enqueue_compress(d, path, cfg, w, hidden, positions, slot_mapping, cache, num_tokens, cp, workspace, s);
+  return finish();
+}
+
+int32_t mla_decode_num_splits(const mla_config* cfg, int32_t batch, int32_t max_blocks) {
+  Dims d;
+  Path path;
+  if (check_config(cfg, &d, &path) != MLA_OK || batch <= 0 || max_blocks <= 0) return 0;
+  return auto_splits(d, path, batch, max_blocks);
+}
+
+size_t mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32_t max_blocks,
+                                 int32_t num_splits) {
+  Dims d;
+  Path path;
+  if (check_config(cfg, &d, &path) != MLA_OK || batch <= 0 || max_blocks <= 0 || num_splits < 0 ||
+      num_splits > 1024)
+    return 0;
+  DecodePlan p;
+  plan_decode(d, path, batch, max_blocks, num_splits, &p);
+  return p.bytes;
+}
+
+int mla_decode(const mla_config* cfg, const mla_weights* w, const void* hidden,
+               const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
+               const mla_cache* cache, int32_t batch, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, void* out, void* stream) {
+  int st = check_decode_args(cfg, w, hidden, context_lens, block_table, max_blocks, cache, batch,
+                             num_splits, out);
+  if (st != MLA_OK) return st;
+  Dims d;
+  Path path;
+  check_config(cfg, &d, &path);
+  DecodePlan p;
+  plan_decode(d, path, batch, max_blocks, num_splits, &p);
+  if (!workspace || workspace_bytes < p.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int act = kdt(cfg->act_dtype);
+  const size_t asz = dtype_size(cfg->act_dtype);
+  const int B = batch;
+  int32_t* pos = reinterpret_cast<int32_t*>(at(workspace, p.off_pos));
+  int64_t* slot = reinterpret_cast<int64_t*>(at(workspace, p.off_slot));
+
+  launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
+  enqueue_compress(d, path, cfg, w, hidden, pos, slot, cache, B, p.comp, workspace, s);
+  enqueue_query(d, path, cfg, w, hidden, B, p.q, workspace, nullptr, 0.f, s);
+
+  // Scaled queries: sigma * log2(e) folded in, so the kernels use exp2.
+  const float qscale = d.sigma * kLog2eHost;
+  void* qnope = at(workspace, p.off_qnope);
+  void* qhat = at(workspace, p.off_qhat);
+  launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n,
+                reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)), pos, qscale, d.theta, qnope, qhat,
+                nullptr, s);
+  // Absorb: qhat[b][h][0:dc] = q_nope[b][h] . W_UK^h  (W_UK^h = kv_b_proj rows of head h's k_nope).
+  launch_gemm(gemm(path, true, act, B, d.dc, d.dn, whole(d.dn), d.H, qnope, long(d.H) * d.dn, d.dn,
+                   w->kv_b_proj, d.dc, long(d.dkv()) * d.dc, qhat, long(d.H) * d.W(), d.W()), s);
+
+  DecodeAttnArgs a;
+  a.B = B; a.H = d.H; a.dc = d.dc; a.dr = d.dr; a.splits = p.splits;
+  a.heads_per_group = decode_heads_per_group(d, path);
+  a.qhat = qhat;
+  a.cache = cache->data; a.cache_scale = cache->scale;
+  a.block_table = block_table; a.max_blocks = max_blocks; a.ctx = context_lens;
+  a.part_o = reinterpret_cast<float*>(at(workspace, p.off_part_o));
+  a.part_ml = reinterpret_cast<float*>(at(workspace, p.off_part_ml));
+  launch_decode_attn(act, kdt(cfg->cache_dtype), a, s);
+
+  void* otilde = at(workspace, p.off_otilde);
+  launch_decode_merge(act, B, d.H, d.dc, p.splits, a.part_o, a.part_ml, otilde, s);
+  // out[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  On the bf16 path
+  // otilde is [hi | lo] (2 dc wide) and both halves are multiplied by the same weight row.
+  const char* w_uv = static_cast<const char*>(w->kv_b_proj) + size_t(d.dn) * d.dc * asz;
+  const int kx = path == PATH_F32 ? d.dc : 2 * d.dc;
+  launch_gemm(gemm(path, false, kdt(cfg->out_dtype), B, d.dv, kx, whole(kx), d.H, otilde, long(d.H) * kx, kx,
+                   w_uv, d.dc, long(d.dkv()) * d.dc, out, long(d.H) * d.dv, d.dv, 1.f,
+                   path == PATH_F32 ? 0 : d.dc), s);
+  return finish();
+}
+
+size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_seqs, int32_t total_tokens,
+                                  int32_t max_q_len, int32_t max_ctx) {
+  Dims d;
+  Path path;
+  if (check_config(cfg, &d, &path) != MLA_OK || num_seqs <= 0 || total_tokens <= 0 || max_q_len <= 0 ||
+      max_ctx <= 0)
+    return 0;
+  PrefillPlan p;
+  plan_prefill(d, path, num_seqs, total_tokens, max_q_len, max_ctx, &p);
+  return p.bytes;
+}
+
+int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                const int32_t* cu_seqlens, const int32_t* start_pos, const int32_t* block_table,
+                int32_t max_blocks, const mla_cache* cache, int32_t num_seqs, int32_t total_tokens,
+                int32_t max_q_len, int32_t max_ctx, void* workspace, size_t workspace_bytes, void* out,
+                void* stream) {
+  int st = check_prefill_args(cfg, w, hidden, cu_seqlens, start_pos, block_table, max_blocks, cache,
+                              num_seqs, total_tokens, max_q_len, max_ctx, out);
+  if (st != MLA_OK) return st;
+  Dims d;
+  Path path;
+  check_config(cfg, &d, &path);
+  PrefillPlan p;
+  plan_prefill(d, path, num_seqs, total_tokens, max_q_len, max_ctx, &p);
+  if (!workspace || workspace_bytes < p.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int act = kdt(cfg->act_dtype);
+  const int T = total_tokens, S = num_seqs;
+  int32_t* pos = reinterpret_cast<int32_t*>(at(workspace, p.off_pos));
+  int64_t* slot = reinterpret_cast<int64_t*>(at(workspace, p.off_slot));
+
+  launch_prefill_prep(S, max_q_len, cu_seqlens, start_pos, block_table, max_blocks, pos, slot, s);
+  enqueue_compress(d, path, cfg, w, hidden, pos, slot, cache, T, p.comp, workspace, s);
+  // Queries scaled by sigma * log2(e), RoPE'd: fp16 on the bf16 path, fp32 on the fp32 path.
+  void* qs = at(workspace, p.off_qs);
+  const float qscale = d.sigma * kLog2eHost;
+  const int qs_type = path == PATH_F32 ? K_F32 : K_F16;
+  enqueue_query(d, path, cfg, w, hidden, T, p.q, workspace, qs, qscale, s);
+  if (p.q.direct)
+    launch_q_rope_f16(T, d.H, d.dn, d.dr, pos, d.theta, qs, s);
+  else
+    launch_q_pack(act, qs_type, false, T, d.H, d.dn, d.dr, d.dc, p.q.split_b.n,
+                  reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)), pos, qscale, d.theta, nullptr,
+                  nullptr, qs, s);
+  void* lat = at(workspace, p.off_lat);
+  launch_gather_rows(act, kdt(cfg->cache_dtype), S, max_ctx, d.W(), cu_seqlens, start_pos, block_table,
+                     max_blocks, cache->data, cache->scale, lat, s);
+  // Decompress every context latent: kv[s][t] = kv_b_proj . latent -> per head [k_nope | v].
+  void* kv = at(workspace, p.off_kv);
+  const long nkv = long(d.H) * d.dkv();
+  launch_gemm(gemm(path, false, K_F16, max_ctx, int(nkv), d.dc, whole(d.dc), S, lat, d.W(),
+                   long(max_ctx) * d.W(), w->kv_b_proj, d.dc, 0, kv, nkv, long(max_ctx) * nkv), s);
+  PrefillAttnArgs a;
+  a.S = S; a.H = d.H; a.dn = d.dn; a.dr = d.dr; a.dv = d.dv; a.dc = d.dc;
+  a.max_q = max_q_len; a.max_ctx = max_ctx; a.out_type = kdt(cfg->out_dtype);
+  a.cu = cu_seqlens; a.start = start_pos;
+  a.qs = qs; a.kv = kv; a.lat = lat; a.out = out;
+  launch_prefill_attn(act, a, s);
+  return finish();
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal launcher interface between the C ABI (mla_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum GemmKind { GEMM_F32 = 0, GEMM_BF16 = 1 };
+
+struct GemmArgs {
+  int kind;                  // GEMM_F32 (fp32 in/out) or GEMM_BF16 (bf16 in, fp32 accumulate)
+  bool nn;                   // W is [K][N] (else [N][K])
+  int out;                   // bf16 path output: K_F32, K_BF16 or K_F16
+  int kwrap;                 // TN only: W column index is k % kwrap (0: k), so X = [x_hi | x_lo]
+                             // of width 2 * kwrap reuses one weight row for both halves
+  int M, N, K;
+  int kchunk, nsplit;        // K split into nsplit slices of kchunk (multiple of 32)
+  int batch;
+  const void* X; long lda, sx;
+  const void* W; long ldw, sw;
+  void* Y; long ldc, sy, ssplit;
+  float alpha;
+};
+void launch_gemm(const GemmArgs& g, hipStream_t st);
+
+// Dtype codes for cache, activations and intermediate buffers inside the kernels.
+enum { K_F32 = 0, K_BF16 = 1, K_FP8 = 2, K_F16 = 3 };
+
+// Cache rows from fp32 kv_a partials: RMSNorm on the latent, RoPE on k_pe, cast, scatter.
+void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit, const float* acc,
+                          const void* gamma, const int32_t* pos, const int64_t* slots,
+                          void* cache_data, float* cache_scale, long num_slots, float eps,
+                          float theta, hipStream_t st);
+
+// out[t][:] = RMSNorm(sum_s acc[s][t][:]) * gamma, in act dtype.
+void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,
+                         void* out, float eps, hipStream_t st);
+
+// Query packing from fp32 partials q_acc [nsplit][T][H*(dn+dr)]: sum, scale by `scale`,
+// RoPE on q_pe.
+//   absorbed: q_nope -> qnope[t][h][dn]; rotated q_pe -> qhat[t][h][dc + i]  (act dtype)
+//   explicit: [q_nope | rotated q_pe] -> qs[t][h][dn + dr]                   (qs_type)
+void launch_q_pack(int act, int qs_type, bool absorbed, int T, int H, int dn, int dr, int dc,
+                   int nsplit, const float* q_acc, const int32_t* pos, float scale, float theta,
+                   void* qnope, void* qhat, void* qs, hipStream_t st);
+// RoPE in place on the q_pe part of fp16 queries qs[t][h][dn + dr] (already scaled).
+void launch_q_rope_f16(int T, int H, int dn, int dr, const int32_t* pos, float theta, void* qs,
+                       hipStream_t st);
+
+void launch_decode_prep(int B, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                        int32_t* pos, int64_t* slot, hipStream_t st);
+void launch_prefill_prep(int S, int max_q, const int32_t* cu, const int32_t* start,
+                         const int32_t* bt, int max_blocks, int32_t* pos, int64_t* slot,
+                         hipStream_t st);
+
+// Split-K decode attention over the latent cache (weight-absorbed form).
+//   qhat [B][H][dc+dr] (pre-scaled by sigma*log2 e), partials o [B][S][H][dc], ml [B][S][H][2]
+struct DecodeAttnArgs {
+  int B, H, dc, dr, splits, heads_per_group;
+  const void* qhat;
+  const void* cache; const float* cache_scale;
+  const int32_t* block_table; int max_blocks;
+  const int32_t* ctx;
+  float* part_o; float* part_ml;
+};
+void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st);
+
+// Log-sum-exp merge of split partials, normalised.  fp32 path: otilde [B][H][dc] fp32; bf16
+// path: otilde [B][H][2*dc] = [hi | lo] with hi = bf16(v), lo = bf16(v - hi).
+void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
+                         const float* part_ml, void* otilde, hipStream_t st);
+
+// Prefill: gather (and dequantise) each sequence's cached rows [0, ctx) into lat [S][max_ctx][W].
+void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, const int32_t* cu,
+                        const int32_t* start, const int32_t* bt, int max_blocks,
+                        const void* cache_data, const float* cache_scale, void* lat,
+                        hipStream_t st);
+
+// Causal attention of packed chunk queries against decompressed keys / values.
+struct PrefillAttnArgs {
+  int S, H, dn, dr, dv, dc, max_q, max_ctx, out_type;
+  const int32_t* cu; const int32_t* start;
+  const void* qs;            // [T][H][dn+dr], pre-scaled by sigma*log2 e (fp16 on the bf16 path)
+  const void* kv;            // [S][max_ctx][H][dn+dv]  (fp16 on the bf16 path)
+  const void* lat;           // [S][max_ctx][dc+dr] act dtype (k_pe at column dc)
+  void* out;                 // [T][H][dv] out_type
+};
+void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,202 @@
+// Host-side argument validation and workspace planning (no HIP dependency).
+#include "mla_plan.h"
+
+#include <cmath>
+
+namespace mla {
+
+namespace {
+inline long cdiv(long a, long b) { return (a + b - 1) / b; }
+inline long rup(long a, long b) { return cdiv(a, b) * b; }
+constexpr long kMaxDim = 1 << 20;
+}  // namespace
+
+size_t dtype_size(int dt) {
+  switch (dt) {
+    case MLA_F32: return 4;
+    case MLA_BF16: return 2;
+    case MLA_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+int check_config(const mla_config* cfg, Dims* d, Path* path) {
+  if (!cfg) return MLA_ERR_INVALID_ARG;
+  const mla_config& c = *cfg;
+  if (c.hidden_size <= 0 || c.num_heads <= 0 || c.q_lora_rank < 0 || c.kv_lora_rank <= 0 ||
+      c.qk_nope_head_dim <= 0 || c.qk_rope_head_dim <= 0 || (c.qk_rope_head_dim & 1) ||
+      c.v_head_dim <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (c.hidden_size > kMaxDim || c.num_heads > 4096 || c.q_lora_rank > kMaxDim ||
+      c.kv_lora_rank > kMaxDim || c.qk_nope_head_dim > kMaxDim || c.qk_rope_head_dim > kMaxDim ||
+      c.v_head_dim > kMaxDim)
+    return MLA_ERR_INVALID_ARG;
+  if (c.page_size != MLA_PAGE_SIZE) return MLA_ERR_INVALID_ARG;
+  if (!(c.rope_theta > 0.f) || !std::isfinite(c.rope_theta)) return MLA_ERR_INVALID_ARG;
+  if (!(c.rms_eps >= 0.f) || !std::isfinite(c.rms_eps)) return MLA_ERR_INVALID_ARG;
+  if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (c.act_dtype != MLA_F32 && c.act_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (dtype_size(c.cache_dtype) == 0) return MLA_ERR_INVALID_ARG;
+  if (c.out_dtype != MLA_F32 && c.out_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+
+  Dims dd;
+  dd.D = c.hidden_size; dd.H = c.num_heads; dd.dq = c.q_lora_rank; dd.dc = c.kv_lora_rank;
+  dd.dn = c.qk_nope_head_dim; dd.dr = c.qk_rope_head_dim; dd.dv = c.v_head_dim;
+  dd.theta = c.rope_theta; dd.eps = c.rms_eps;
+  dd.sigma = c.softmax_scale > 0.f ? c.softmax_scale
+                                   : 1.0f / std::sqrt(float(dd.dn + dd.dr));
+  Path p = PATH_NONE;
+  if (c.act_dtype == MLA_F32 && c.cache_dtype == MLA_F32 && c.out_dtype == MLA_F32) {
+    if (dd.dc <= 4096 && dd.dr <= 256 && dd.dn <= 4096 && dd.dv <= 4096) p = PATH_F32;
+  } else if (c.act_dtype == MLA_BF16 &&
+             (c.cache_dtype == MLA_BF16 || c.cache_dtype == MLA_FP8_E4M3)) {
+    if (dd.dc == 512 && dd.dr == 64 && dd.dn == 128 && dd.dv == 128 && dd.H % 16 == 0 &&
+        dd.D % 8 == 0 && dd.dq % 8 == 0)
+      p = PATH_BF16;
+  }
+  if (p == PATH_NONE) return MLA_ERR_UNSUPPORTED;
+  if (d) *d = dd;
+  if (path) *path = p;
+  return MLA_OK;
+}
+
+SplitK gemm_splitk(long M, long N, long K, int tile_m, int tile_n) {
+  long tiles = cdiv(M, tile_m) * cdiv(N, tile_n);
+  SplitK s{1, int(rup(K, 32))};
+  if (tiles >= 192 || K < 512) return s;
+  long want = cdiv(256, tiles);
+  long most = K / 256;
+  long n = want < most ? want : most;
+  if (n <= 1) return s;
+  long chunk = rup(cdiv(K, n), 32);
+  s.n = int(cdiv(K, chunk));
+  s.chunk = int(chunk);
+  return s;
+}
+
+int plan_compress(const Dims& d, Path path, long T, Layout& L, CompressPlan* p) {
+  (void)path;
+  p->split = gemm_splitk(T, d.W(), d.D, 64, 64);
+  p->off_acc = L.take(size_t(p->split.n) * T * d.W() * 4);
+  return MLA_OK;
+}
+
+static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q, bool allow_direct) {
+  long nq = long(d.H) * d.dqk();
+  if (d.dq > 0) {
+    q->split_a = gemm_splitk(T, d.dq, d.D, 64, 64);
+    q->off_qa_acc = L.take(size_t(q->split_a.n) * T * d.dq * 4);
+    q->off_cq = L.take(size_t(T) * d.dq * (path == PATH_F32 ? 4 : 2));
+    q->split_b = gemm_splitk(T, nq, d.dq, 64, 64);
+  } else {
+    q->split_a = SplitK{1, 32};
+    q->off_qa_acc = q->off_cq = 0;
+    q->split_b = gemm_splitk(T, nq, d.D, 64, 64);
+  }
+  q->direct = allow_direct && path == PATH_BF16 && q->split_b.n == 1;
+  q->off_q_acc = q->direct ? 0 : L.take(size_t(q->split_b.n) * T * nq * 4);
+}
+
+int decode_heads_per_group(const Dims& d, Path path) {
+  if (path != PATH_BF16) return 1;
+  for (int g = 64; g >= 16; g /= 2)
+    if (d.H % g == 0) return g;
+  return 16;
+}
+
+int auto_splits(const Dims& d, Path path, int B, int max_blocks) {
+  long groups = d.H / decode_heads_per_group(d, path);
+  long wgs = long(B) * groups;
+  long target = path == PATH_BF16 ? 256 : 512;
+  long s = cdiv(target, wgs);
+  long most = max_blocks / 2 > 1 ? max_blocks / 2 : 1;
+  if (s > most) s = most;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  return int(s);
+}
+
+int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, DecodePlan* p) {
+  Layout L;
+  p->splits = splits > 0 ? splits : auto_splits(d, path, B, max_blocks);
+  size_t act = path == PATH_F32 ? 4 : 2;
+  plan_compress(d, path, B, L, &p->comp);
+  plan_query(d, path, B, L, &p->q, false);
+  p->off_pos = L.take(size_t(B) * 4);
+  p->off_slot = L.take(size_t(B) * 8);
+  p->off_qnope = L.take(size_t(B) * d.H * d.dn * act);
+  p->off_qhat = L.take(size_t(B) * d.H * d.W() * act);
+  p->off_part_o = L.take(size_t(B) * p->splits * d.H * d.dc * 4);
+  p->off_part_ml = L.take(size_t(B) * p->splits * d.H * 2 * 4);
+  p->off_otilde = L.take(size_t(B) * d.H * d.dc * (path == PATH_F32 ? 4 : 2 * 2));
+  p->bytes = L.top;
+  return MLA_OK;
+}
+
+int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, PrefillPlan* p) {
+  (void)max_q;
+  Layout L;
+  size_t act = path == PATH_F32 ? 4 : 2;
+  plan_compress(d, path, T, L, &p->comp);
+  plan_query(d, path, T, L, &p->q, true);
+  p->off_pos = L.take(size_t(T) * 4);
+  p->off_slot = L.take(size_t(T) * 8);
+  p->off_qs = L.take(size_t(T) * d.H * d.dqk() * act);
+  p->off_lat = L.take(size_t(S) * max_ctx * d.W() * act);
+  p->off_kv = L.take(size_t(S) * max_ctx * d.H * d.dkv() * act);
+  p->bytes = L.top;
+  return MLA_OK;
+}
+
+static bool cache_ok(const mla_config* cfg, const mla_cache* cache) {
+  if (!cache || !cache->data || cache->num_blocks <= 0) return false;
+  if (cfg->cache_dtype == MLA_FP8_E4M3 && !cache->scale) return false;
+  return true;
+}
+
+static bool query_weights_ok(const mla_config* cfg, const mla_weights* w) {
+  if (!w || !w->q_b_proj || !w->kv_a_proj || !w->kv_a_norm || !w->kv_b_proj) return false;
+  if (cfg->q_lora_rank > 0 && (!w->q_a_proj || !w->q_a_norm)) return false;
+  return true;
+}
+
+int check_compress_args(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                        const int32_t* positions, const int64_t* slots, const mla_cache* cache,
+                        int32_t T) {
+  int st = check_config(cfg, nullptr, nullptr);
+  if (st != MLA_OK) return st;
+  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (!w || !w->kv_a_proj || !w->kv_a_norm) return MLA_ERR_INVALID_ARG;
+  if (!cache_ok(cfg, cache)) return MLA_ERR_INVALID_ARG;
+  if (T > 0 && (!hidden || !positions || !slots)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int check_decode_args(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                      const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
+                      const mla_cache* cache, int32_t B, int32_t splits, const void* out) {
+  int st = check_config(cfg, nullptr, nullptr);
+  if (st != MLA_OK) return st;
+  if (B <= 0 || max_blocks <= 0 || splits < 0 || splits > 1024) return MLA_ERR_INVALID_ARG;
+  if (long(B) * max_blocks > (1L << 30)) return MLA_ERR_INVALID_ARG;
+  if (!query_weights_ok(cfg, w) || !cache_ok(cfg, cache)) return MLA_ERR_INVALID_ARG;
+  if (!hidden || !context_lens || !block_table || !out) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int check_prefill_args(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                       const int32_t* cu_seqlens, const int32_t* start_pos,
+                       const int32_t* block_table, int32_t max_blocks, const mla_cache* cache,
+                       int32_t S, int32_t T, int32_t max_q, int32_t max_ctx, const void* out) {
+  int st = check_config(cfg, nullptr, nullptr);
+  if (st != MLA_OK) return st;
+  if (S <= 0 || T <= 0 || max_q <= 0 || max_ctx <= 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (max_q > T || max_q > max_ctx) return MLA_ERR_INVALID_ARG;
+  if (long(max_ctx) > long(max_blocks) * MLA_PAGE_SIZE) return MLA_ERR_INVALID_ARG;
+  if (long(S) * max_blocks > (1L << 30) || long(S) * max_ctx > (1L << 30)) return MLA_ERR_INVALID_ARG;
+  if (!query_weights_ok(cfg, w) || !cache_ok(cfg, cache)) return MLA_ERR_INVALID_ARG;
+  if (!hidden || !cu_seqlens || !start_pos || !block_table || !out) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+}  // namespace mla

@@ -1,0 +1,104 @@
+// Host-side argument validation and workspace planning for libmla.  No HIP dependency: this
+// translation unit also builds with a plain host compiler for sanitizer tests on the CPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "mla.h"
+
+namespace mla {
+
+enum Path { PATH_NONE = 0, PATH_F32 = 1, PATH_BF16 = 2 };
+
+struct Dims {
+  int D, H, dq, dc, dn, dr, dv;
+  int W() const { return dc + dr; }      // cached row width
+  int dqk() const { return dn + dr; }    // per-head query width
+  int dkv() const { return dn + dv; }    // per-head kv_b_proj rows
+  float theta, eps, sigma;
+};
+
+// Element size in bytes of an mla_dtype (0 for an unknown code).
+size_t dtype_size(int dt);
+
+// Validates the configuration; fills dims and the kernel path.  Returns a status.
+int check_config(const mla_config* cfg, Dims* d, Path* path);
+
+// A bump allocator over one workspace: every region 256-byte aligned.
+struct Layout {
+  size_t top = 0;
+  size_t take(size_t bytes) {
+    size_t off = top;
+    top += (bytes + 255) & ~size_t(255);
+    return off;
+  }
+};
+
+// Split-K of a GEMM's K range so that an M x N output grid covers the GPU: `n` slices of
+// `chunk` (a multiple of 32) K values each; the last slice may be shorter.
+struct SplitK {
+  int n;
+  int chunk;
+};
+SplitK gemm_splitk(long M, long N, long K, int tile_m, int tile_n);
+
+struct CompressPlan {
+  SplitK split;
+  size_t off_acc;        // fp32 [split.n][T][W]
+};
+int plan_compress(const Dims& d, Path path, long T, Layout& L, CompressPlan* p);
+
+struct QueryPlan {            // q path for T tokens, shared by decode and prefill
+  SplitK split_a, split_b;
+  bool direct;                // prefill, bf16 path, no K split: the q projection writes the
+                              // scaled fp16 queries straight into their final buffer
+  size_t off_qa_acc;          // fp32 [split_a.n][T][dq]          (dq > 0)
+  size_t off_cq;              // act  [T][dq]                      (dq > 0)
+  size_t off_q_acc;           // fp32 [split_b.n][T][H*dqk]        (!direct)
+};
+
+// Heads one decode work-group serves (bf16 path: a multiple of 16 dividing H).
+int decode_heads_per_group(const Dims& d, Path path);
+
+struct DecodePlan {
+  int splits;
+  CompressPlan comp;
+  QueryPlan q;
+  size_t off_pos;             // int32 [B]
+  size_t off_slot;            // int64 [B]
+  size_t off_qnope;           // act  [B][H][dn]   scaled q_nope
+  size_t off_qhat;            // act  [B][H][W]    absorbed, scaled query
+  size_t off_part_o;          // fp32 [B][splits][H][dc]
+  size_t off_part_ml;         // fp32 [B][splits][H][2]
+  size_t off_otilde;          // f32 [B][H][dc], or bf16 [B][H][2*dc] = [hi | lo] halves
+  size_t bytes;
+};
+int auto_splits(const Dims& d, Path path, int B, int max_blocks);
+int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, DecodePlan* p);
+
+struct PrefillPlan {
+  CompressPlan comp;
+  QueryPlan q;
+  size_t off_pos;             // int32 [T]
+  size_t off_slot;            // int64 [T]
+  size_t off_qs;              // [T][H][dqk] scaled, RoPE'd queries (fp32; fp16 on the bf16 path)
+  size_t off_lat;             // act  [S][max_ctx][W] gathered (dequantised) cache rows
+  size_t off_kv;              // [S][max_ctx][H*dkv] decompressed k_nope | v (fp32; fp16 on the bf16 path)
+  size_t bytes;
+};
+int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, PrefillPlan* p);
+
+// Per-call argument checks (pointers, sizes); return a status.
+int check_compress_args(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                        const int32_t* positions, const int64_t* slots, const mla_cache* cache,
+                        int32_t T);
+int check_decode_args(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                      const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
+                      const mla_cache* cache, int32_t B, int32_t splits, const void* out);
+int check_prefill_args(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                       const int32_t* cu_seqlens, const int32_t* start_pos,
+                       const int32_t* block_table, int32_t max_blocks, const mla_cache* cache,
+                       int32_t S, int32_t T, int32_t max_q, int32_t max_ctx, const void* out);
+
+}  // namespace mla
