@@ -144,6 +144,16 @@ int mla_decode(const mla_config *cfg, const mla_weights *w, const void *hidden,
                const mla_cache *cache, int32_t batch, int32_t num_splits, void *workspace,
                size_t workspace_bytes, void *out, void *stream);
 
+/* mla_decode, and additionally records two caller-created hipEvent_t handles on `stream`:
+ * `ev_attn_begin` just before the split-K attention kernel is enqueued and `ev_attn_end` just
+ * after it, so hipEventElapsedTime gives that kernel's duration.  Either may be NULL.  For
+ * timing and profiling; results are identical to mla_decode. */
+int mla_decode_timed(const mla_config *cfg, const mla_weights *w, const void *hidden,
+                     const int32_t *context_lens, const int32_t *block_table, int32_t max_blocks,
+                     const mla_cache *cache, int32_t batch, int32_t num_splits, void *workspace,
+                     size_t workspace_bytes, void *out, void *stream, void *ev_attn_begin,
+                     void *ev_attn_end);
+
 /* ---------------------------------------------------------------------------------------
  * mla_prefill: causal prefill of one chunk per sequence, explicit (decompressing) form.
  * Page section "源码里的压缩全流程" end to end: the chunk's tokens are compressed and

@@ -53,6 +53,8 @@ SIGNATURES = {
     "mla_decode_workspace_size": (_sz, [_P(MlaConfig), _i32, _i32, _i32]),
     "mla_decode": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _i32, _P(MlaCache), _i32, _i32,
                                   _vp, _sz, _vp, _vp]),
+    "mla_decode_timed": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
+                                        _i32, _vp, _sz, _vp, _vp, _vp, _vp]),
     "mla_prefill_workspace_size": (_sz, [_P(MlaConfig), _i32, _i32, _i32, _i32]),
     "mla_prefill": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                    _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
@@ -166,7 +168,8 @@ def decode_workspace_size(cfg, batch, max_blocks, num_splits=0):
 
 
 def decode(cfg, weights, hidden, context_lens, block_table, cache, num_splits=0, out=None, workspace=None,
-           stream=None, weights_struct=None):
+           stream=None, weights_struct=None, attn_events=None):
+    """attn_events: optional (begin, end) hipEvent_t handles recorded around the attention kernel."""
     L = lib()
     B, max_blocks = block_table.shape
     nbytes = L.mla_decode_workspace_size(ctypes.byref(cfg), B, max_blocks, num_splits)
@@ -175,9 +178,15 @@ def decode(cfg, weights, hidden, context_lens, block_table, cache, num_splits=0,
         out = torch.empty((B, cfg.num_heads, cfg.v_head_dim), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
     W = weights_struct if weights_struct is not None else make_weights(weights)
     cs = cache.struct()
-    _check(L.mla_decode(ctypes.byref(cfg), ctypes.byref(W), _ptr(hidden), _ptr(context_lens), _ptr(block_table),
-                        max_blocks, ctypes.byref(cs), B, num_splits, _ptr(ws), nbytes, _ptr(out), _stream(stream)),
-           "mla_decode")
+    if attn_events is None:
+        _check(L.mla_decode(ctypes.byref(cfg), ctypes.byref(W), _ptr(hidden), _ptr(context_lens),
+                            _ptr(block_table), max_blocks, ctypes.byref(cs), B, num_splits, _ptr(ws), nbytes,
+                            _ptr(out), _stream(stream)), "mla_decode")
+    else:
+        _check(L.mla_decode_timed(ctypes.byref(cfg), ctypes.byref(W), _ptr(hidden), _ptr(context_lens),
+                                  _ptr(block_table), max_blocks, ctypes.byref(cs), B, num_splits, _ptr(ws), nbytes,
+                                  _ptr(out), _stream(stream), ctypes.c_void_p(attn_events[0]),
+                                  ctypes.c_void_p(attn_events[1])), "mla_decode_timed")
     return out
 
 

@@ -138,10 +138,11 @@ size_t mla_decode_workspace_size(const mla_config* cfg, int32_t batch, int32_t m
   return p.bytes;
 }
 
-int mla_decode(const mla_config* cfg, const mla_weights* w, const void* hidden,
-               const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
-               const mla_cache* cache, int32_t batch, int32_t num_splits, void* workspace,
-               size_t workspace_bytes, void* out, void* stream) {
+int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                     const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
+                     const mla_cache* cache, int32_t batch, int32_t num_splits, void* workspace,
+                     size_t workspace_bytes, void* out, void* stream, void* ev_attn_begin,
+                     void* ev_attn_end) {
   int st = check_decode_args(cfg, w, hidden, context_lens, block_table, max_blocks, cache, batch,
                              num_splits, out);
   if (st != MLA_OK) return st;
@@ -182,7 +183,9 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* hidden,
   a.block_table = block_table; a.max_blocks = max_blocks; a.ctx = context_lens;
   a.part_o = reinterpret_cast<float*>(at(workspace, p.off_part_o));
   a.part_ml = reinterpret_cast<float*>(at(workspace, p.off_part_ml));
+  if (ev_attn_begin) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_begin), s);
   launch_decode_attn(act, kdt(cfg->cache_dtype), a, s);
+  if (ev_attn_end) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_end), s);
 
   void* otilde = at(workspace, p.off_otilde);
   launch_decode_merge(act, B, d.H, d.dc, p.splits, a.part_o, a.part_ml, otilde, s);
@@ -194,6 +197,14 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* hidden,
                    w_uv, d.dc, long(d.dkv()) * d.dc, out, long(d.H) * d.dv, d.dv, 1.f,
                    path == PATH_F32 ? 0 : d.dc), s);
   return finish();
+}
+
+int mla_decode(const mla_config* cfg, const mla_weights* w, const void* hidden,
+               const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
+               const mla_cache* cache, int32_t batch, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, void* out, void* stream) {
+  return mla_decode_timed(cfg, w, hidden, context_lens, block_table, max_blocks, cache, batch, num_splits,
+                          workspace, workspace_bytes, out, stream, nullptr, nullptr);
 }
 
 size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_seqs, int32_t total_tokens,

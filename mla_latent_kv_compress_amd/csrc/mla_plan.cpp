@@ -43,6 +43,7 @@ int check_config(const mla_config* cfg, Dims* d, Path* path) {
   dd.D = c.hidden_size; dd.H = c.num_heads; dd.dq = c.q_lora_rank; dd.dc = c.kv_lora_rank;
   dd.dn = c.qk_nope_head_dim; dd.dr = c.qk_rope_head_dim; dd.dv = c.v_head_dim;
   dd.theta = c.rope_theta; dd.eps = c.rms_eps;
+  dd.cache_dt = c.cache_dtype;
   dd.sigma = c.softmax_scale > 0.f ? c.softmax_scale
                                    : 1.0f / std::sqrt(float(dd.dn + dd.dr));
   Path p = PATH_NONE;
@@ -99,6 +100,7 @@ static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q
 
 int decode_heads_per_group(const Dims& d, Path path) {
   if (path != PATH_BF16) return 1;
+  if (d.cache_dt == MLA_BF16 && d.H % 128 == 0) return 128;
   for (int g = 64; g >= 16; g /= 2)
     if (d.H % g == 0) return g;
   return 16;

@@ -13,6 +13,7 @@ enum Path { PATH_NONE = 0, PATH_F32 = 1, PATH_BF16 = 2 };
 
 struct Dims {
   int D, H, dq, dc, dn, dr, dv;
+  int cache_dt;                          // mla_dtype of the cache
   int W() const { return dc + dr; }      // cached row width
   int dqk() const { return dn + dr; }    // per-head query width
   int dkv() const { return dn + dv; }    // per-head kv_b_proj rows
@@ -58,7 +59,8 @@ struct QueryPlan {            // q path for T tokens, shared by decode and prefi
   size_t off_q_acc;           // fp32 [split_b.n][T][H*dqk]        (!direct)
 };
 
-// Heads one decode work-group serves (bf16 path: a multiple of 16 dividing H).
+// Heads one decode work-group serves: 128 for a bf16 cache with H % 128 == 0 (one work-group
+// per sequence split), else the largest of 64/32/16 dividing H (bf16 path), 1 (fp32 path).
 int decode_heads_per_group(const Dims& d, Path path);
 
 struct DecodePlan {

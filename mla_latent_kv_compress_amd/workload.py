@@ -88,8 +88,8 @@ class DecodeBatch:
         self.ctx_t = torch.as_tensor(self.ctx.astype(np.int32), device=layer.device)
         self.table_t = torch.as_tensor(self.table, device=layer.device)
 
-    def run(self, num_splits=None, out=None, workspace=None, stream=None):
+    def run(self, num_splits=None, out=None, workspace=None, stream=None, attn_events=None):
         s = self.wl.num_splits if num_splits is None else num_splits
         return api.decode(self.layer.cfg, self.layer.w, self.x, self.ctx_t, self.table_t, self.cache,
                           num_splits=s, out=out, workspace=workspace, stream=stream,
-                          weights_struct=self.layer.w_struct)
+                          weights_struct=self.layer.w_struct, attn_events=attn_events)

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     L = api.lib()
     for n in names:
         assert hasattr(L, n), n
