@@ -5,6 +5,22 @@
 
 namespace mla {
 
+// Sum of the K-split partials acc[s * stride + i], s = 0 .. n-1, in split order.  Eight loads are
+// issued before the adds so the chain is not one memory latency per split.
+__device__ __forceinline__ float split_sum(const float* __restrict__ acc, int n, long stride, long i) {
+  float v = 0.f;
+  int s = 0;
+  for (; s + 8 <= n; s += 8) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = acc[(s + j) * stride + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += x[j];
+  }
+  for (; s < n; ++s) v += acc[s * stride + i];
+  return v;
+}
+
 // ------------------------------------------------------------------ compress epilogue
 // One block per token.  a = sum of the kv_a partials = [latent (dc) | k_pe (dr)].
 // latent <- latent / sqrt(mean(latent^2) + eps) * gamma;  k_pe <- RoPE(k_pe, pos);
@@ -19,11 +35,7 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
   const int t = blockIdx.x, W = dc + dr;
   const long slot = slots[t];
   if (slot < 0 || slot >= num_slots) return;        // uniform over the block
-  for (int i = threadIdx.x; i < W; i += blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += acc[(long(s) * T + t) * W + i];
-    row[i] = v;
-  }
+  for (int i = threadIdx.x; i < W; i += blockDim.x) row[i] = split_sum(acc, nsplit, long(T) * W, long(t) * W + i);
   __syncthreads();
   float ss = 0.f;
   for (int i = threadIdx.x; i < dc; i += blockDim.x) ss += row[i] * row[i];
@@ -87,8 +99,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsp
   const int t = blockIdx.x;
   float ss = 0.f;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += acc[(long(s) * T + t) * n + i];
+    const float v = split_sum(acc, nsplit, long(T) * n, long(t) * n + i);
     row[i] = v;
     ss += v * v;
   }
@@ -111,8 +122,11 @@ void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, co
 }
 
 // ------------------------------------------------------------------ query packing
-// Block per token; thread loop over heads x (nope values + rope pairs).  ACT is the absorbed
-// outputs' storage, QS the explicit output's.
+// Block per (token, group of kQH heads): the RoPE angles of the token's position are formed
+// once per block (fp64 phase) in shared memory; threads then loop over the group's values.
+// ACT is the absorbed outputs' storage, QS the explicit output's.
+constexpr int kQH = 4;
+
 template <int ACT, int QS>
 __global__ __launch_bounds__(256) void q_pack_kernel(bool absorbed, int T, int H, int dn, int dr, int dc,
                                                      int nsplit, const float* __restrict__ q_acc,
@@ -120,18 +134,17 @@ __global__ __launch_bounds__(256) void q_pack_kernel(bool absorbed, int T, int H
                                                      typename StoreT<ACT>::type* __restrict__ qnope,
                                                      typename StoreT<ACT>::type* __restrict__ qhat,
                                                      typename StoreT<QS>::type* __restrict__ qs) {
-  const int t = blockIdx.x;
+  extern __shared__ float cs[];                      // [dr/2] cos | [dr/2] sin
+  const int t = blockIdx.x, h_lo = blockIdx.y * kQH;
   const int dqk = dn + dr, half = dr / 2;
   const long nq = long(H) * dqk;
   const int per_head = dn + half;
-  const int p = pos[t];
-  auto q_at = [&](long j) -> float {
-    float v = 0.f;
-    for (int s = 0; s < nsplit; ++s) v += q_acc[(long(s) * T + t) * nq + j];
-    return v;
-  };
-  for (int e = threadIdx.x; e < H * per_head; e += blockDim.x) {
-    const int h = e / per_head, i = e % per_head;
+  const int nh = min(kQH, H - h_lo);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(pos[t], i, dr, theta, &cs[i], &cs[half + i]);
+  __syncthreads();
+  auto q_at = [&](long j) -> float { return split_sum(q_acc, nsplit, long(T) * nq, long(t) * nq + j); };
+  for (int e = threadIdx.x; e < nh * per_head; e += blockDim.x) {
+    const int h = h_lo + e / per_head, i = e % per_head;
     const long base = long(h) * dqk;
     if (i < dn) {
       float v = scale * q_at(base + i);
@@ -139,10 +152,9 @@ __global__ __launch_bounds__(256) void q_pack_kernel(bool absorbed, int T, int H
       else sts_<QS>(qs, (long(t) * H + h) * dqk + i, v);
     } else {
       const int pi = i - dn;
-      float c, s;
-      rope_cs(p, pi, dr, theta, &c, &s);
+      const float c = cs[pi], sn = cs[half + pi];
       float ev = q_at(base + dn + 2 * pi), ov = q_at(base + dn + 2 * pi + 1);
-      float re = scale * (ev * c - ov * s), ro = scale * (ev * s + ov * c);
+      float re = scale * (ev * c - ov * sn), ro = scale * (ev * sn + ov * c);
       if (absorbed) {
         long o = (long(t) * H + h) * (dc + dr) + dc + 2 * pi;
         sts_<ACT>(qhat, o, re);
@@ -160,29 +172,33 @@ void launch_q_pack(int act, int qs_type, bool absorbed, int T, int H, int dn, in
                    const float* q_acc, const int32_t* pos, float scale, float theta, void* qnope, void* qhat,
                    void* qs, hipStream_t st) {
   if (T <= 0) return;
+  dim3 grid(T, (H + kQH - 1) / kQH);
+  size_t sh = size_t(dr) * sizeof(float);
   if (act == K_F32)
-    hipLaunchKernelGGL((q_pack_kernel<S_F32, S_F32>), dim3(T), dim3(256), 0, st, absorbed, T, H, dn, dr, dc,
+    hipLaunchKernelGGL((q_pack_kernel<S_F32, S_F32>), grid, dim3(256), sh, st, absorbed, T, H, dn, dr, dc,
                        nsplit, q_acc, pos, scale, theta, static_cast<float*>(qnope), static_cast<float*>(qhat),
                        static_cast<float*>(qs));
   else if (qs_type == K_F16)
-    hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_F16>), dim3(T), dim3(256), 0, st, absorbed, T, H, dn, dr, dc,
+    hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_F16>), grid, dim3(256), sh, st, absorbed, T, H, dn, dr, dc,
                        nsplit, q_acc, pos, scale, theta, static_cast<uint16_t*>(qnope),
                        static_cast<uint16_t*>(qhat), static_cast<uint16_t*>(qs));
   else
-    hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_BF16>), dim3(T), dim3(256), 0, st, absorbed, T, H, dn, dr, dc,
+    hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_BF16>), grid, dim3(256), sh, st, absorbed, T, H, dn, dr, dc,
                        nsplit, q_acc, pos, scale, theta, static_cast<uint16_t*>(qnope),
                        static_cast<uint16_t*>(qhat), static_cast<uint16_t*>(qs));
 }
 
 // In-place RoPE of the q_pe part of fp16 queries (the projection already wrote them scaled).
+// Block per token; the token's angles are formed once in shared memory.
 __global__ __launch_bounds__(256) void q_rope_f16_kernel(int H, int dn, int dr, const int32_t* __restrict__ pos,
                                                          float theta, uint16_t* __restrict__ qs) {
+  extern __shared__ float cs[];
   const int t = blockIdx.x, half = dr / 2, dqk = dn + dr;
-  const int p = pos[t];
+  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(pos[t], i, dr, theta, &cs[i], &cs[half + i]);
+  __syncthreads();
   for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
     const int h = e / half, pi = e % half;
-    float c, s;
-    rope_cs(p, pi, dr, theta, &c, &s);
+    const float c = cs[pi], s = cs[half + pi];
     uint16_t* q = qs + (long(t) * H + h) * dqk + dn + 2 * pi;
     float ev = h2f(q[0]), ov = h2f(q[1]);
     q[0] = f2h(ev * c - ov * s);
@@ -192,7 +208,8 @@ __global__ __launch_bounds__(256) void q_rope_f16_kernel(int H, int dn, int dr, 
 
 void launch_q_rope_f16(int T, int H, int dn, int dr, const int32_t* pos, float theta, void* qs, hipStream_t st) {
   if (T <= 0) return;
-  hipLaunchKernelGGL(q_rope_f16_kernel, dim3(T), dim3(256), 0, st, H, dn, dr, pos, theta, static_cast<uint16_t*>(qs));
+  hipLaunchKernelGGL(q_rope_f16_kernel, dim3(T), dim3(256), size_t(dr) * sizeof(float), st, H, dn, dr, pos, theta,
+                     static_cast<uint16_t*>(qs));
 }
 
 // ------------------------------------------------------------------ positions and slots
@@ -239,22 +256,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int sp
                                                            const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            void* __restrict__ otilde) {
+  extern __shared__ float wts[];                    // [splits] normalised split weights
+  __shared__ float red[16];
   const int h = blockIdx.x, b = blockIdx.y;
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, part_ml[((long(b) * splits + s) * H + h) * 2]);
+  for (int s = threadIdx.x; s < splits; s += blockDim.x) m = fmaxf(m, part_ml[((long(b) * splits + s) * H + h) * 2]);
+  m = block_max(m, red);
   float l = 0.f;
-  for (int s = 0; s < splits; ++s) {
+  for (int s = threadIdx.x; s < splits; s += blockDim.x) {
     const float* ml = part_ml + ((long(b) * splits + s) * H + h) * 2;
-    if (ml[0] != -INFINITY) l += exp2f(ml[0] - m) * ml[1];
+    const float w = ml[0] == -INFINITY ? 0.f : exp2f(ml[0] - m);
+    wts[s] = w;
+    l += w * ml[1];
   }
+  l = block_sum(l, red);                            // also orders the wts writes before the reads
   const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const long stride = long(H) * dc;                 // between consecutive splits of one (b, h)
+  const float* po = part_o + (long(b) * splits * H + h) * dc;
   for (int c = threadIdx.x; c < dc; c += blockDim.x) {
     float v = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const long base = (long(b) * splits + s) * H + h;
-      float ms = part_ml[base * 2];
-      if (ms != -INFINITY) v += exp2f(ms - m) * part_o[base * dc + c];
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = po[(s + j) * stride + c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v += wts[s + j] * x[j];
     }
+    for (; s < splits; ++s) v += wts[s] * po[s * stride + c];
     v *= inv;
     if (HILO) {
       uint16_t* o = static_cast<uint16_t*>(otilde) + (long(b) * H + h) * 2 * dc;
@@ -270,11 +299,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int sp
 void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
                          const float* part_ml, void* otilde, hipStream_t st) {
   if (act == K_F32)
-    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(H, B), dim3(256), 0, st, H, dc, splits, part_o, part_ml,
-                       otilde);
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(H, B), dim3(256), size_t(splits) * 4, st, H, dc, splits,
+                       part_o, part_ml, otilde);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(H, B), dim3(256), 0, st, H, dc, splits, part_o, part_ml,
-                       otilde);
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(H, B), dim3(256), size_t(splits) * 4, st, H, dc, splits,
+                       part_o, part_ml, otilde);
 }
 
 // ------------------------------------------------------------------ prefill gather

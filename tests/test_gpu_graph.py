@@ -1,0 +1,39 @@
+"""A decode step captured in a HIP graph replays to the eager result, every replay."""
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_compress_amd import api
+from mla_latent_kv_compress_amd.configs import DSV2, TINY, Workload
+from mla_latent_kv_compress_amd.workload import DecodeBatch, Layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("shape,act,cache", [(DSV2, "bf16", "bf16"), (DSV2, "bf16", "fp8"), (TINY, "f32", "f32")])
+def test_graph_replays_match_eager(shape, act, cache):
+    print(f"graph replay {act}/{cache}", flush=True)
+    layer = Layer(shape, act, cache, seed=11)
+    batch = DecodeBatch(layer, Workload("g", shape, act, cache, decode_batch=3), seed=11, lengths=[70, 300, 1])
+    splits = 3
+    B, mb = batch.table.shape
+    ws = torch.empty(api.decode_workspace_size(layer.cfg, B, mb, splits), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, shape.num_heads, shape.v_head_dim), dtype=torch.float32, device="cuda")
+    ref = batch.run(num_splits=splits, out=torch.empty_like(out), workspace=ws).clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        batch.run(num_splits=splits, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        batch.run(num_splits=splits, out=out, workspace=ws)
+    scratch = torch.randn(1 << 20, device="cuda")
+    for i in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        scratch.mul_(1.0001).add_(0.5)            # the program's own eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager result"
