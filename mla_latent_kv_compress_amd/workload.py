@@ -59,7 +59,9 @@ def build_history(layer, cache, table, lengths, seed=0, chunk=8192, threads=None
 
     ws = None
     with ThreadPoolExecutor(threads) as ex:
-        for b, L, hid in ex.map(gen, jobs):
+        # jobs go to the pool a window at a time so that at most `threads` histories are held
+        done = (r for i in range(0, len(jobs), threads) for r in ex.map(gen, jobs[i:i + threads]))
+        for b, L, hid in done:
             for s in range(0, L, chunk):
                 n = min(chunk, L - s)
                 pos = np.arange(s, s + n)
@@ -93,3 +95,36 @@ class DecodeBatch:
         return api.decode(self.layer.cfg, self.layer.w, self.x, self.ctx_t, self.table_t, self.cache,
                           num_splits=s, out=out, workspace=workspace, stream=stream,
                           weights_struct=self.layer.w_struct, attn_events=attn_events)
+
+
+class PrefillBatch:
+    """Chunked prefill of S prompts of `length` tokens each, in chunks of `chunk` tokens.
+
+    The prompts are the seeded prefill hidden states (inputs.prefill_hidden); every sequence
+    starts empty and chunk k of every sequence goes into one mla_prefill call.
+    """
+
+    def __init__(self, layer, num_seqs, length, chunk, seed=0, shuffle=True):
+        self.layer, self.S, self.length, self.chunk, self.seed = layer, num_seqs, length, chunk, seed
+        self.table, self.num_blocks = inputs.block_table(np.full(num_seqs, length), seed, shuffle=shuffle)
+        self.cache = layer.new_cache(self.num_blocks)
+        self.table_t = torch.as_tensor(self.table, device=layer.device)
+        self.prompts = [inputs.prefill_hidden(layer.shape, s, length, layer.act, seed) for s in range(num_seqs)]
+        self.num_chunks = (length + chunk - 1) // chunk
+        self._dev = []
+        for k in range(self.num_chunks):
+            c0, c1 = k * chunk, min(length, (k + 1) * chunk)
+            x = np.concatenate([p[c0:c1] for p in self.prompts])
+            cu = np.arange(num_seqs + 1, dtype=np.int32) * (c1 - c0)
+            self._dev.append((to_device(x, layer.act, layer.device), torch.as_tensor(cu, device=layer.device),
+                              torch.full((num_seqs,), c0, dtype=torch.int32, device=layer.device), c1 - c0, c1))
+
+    def workspace_size(self):
+        k = self.num_chunks - 1
+        _, _, _, n, c1 = self._dev[k]
+        return api.prefill_workspace_size(self.layer.cfg, self.S, self.S * n, n, c1)
+
+    def run_chunk(self, k, out=None, workspace=None, stream=None):
+        x, cu, start, n, c1 = self._dev[k]
+        return api.prefill(self.layer.cfg, self.layer.w, x, cu, start, self.table_t, self.cache, n, c1,
+                           out=out, workspace=workspace, stream=stream)
