@@ -174,6 +174,243 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     }
 }
 
+// ------------------------------------------------------------------ skinny bf16 GEMM (M <= 64)
+// Y = alpha X W^T for M <= 64 rows (a decode batch): the weight stream is the whole cost, so
+// each work-group owns 64 output columns and streams its [64 x K-chunk] slice of W (and the
+// matching slice of X, an L2 hit) through a ring of kSkStages LDS stages with direct
+// global->LDS loads, several stages ahead of the MFMAs.  A stage is 64 rows x 64 k of X and of W,
+// rows of 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), so the 16 rows
+// of an MFMA operand read fall on distinct banks.  Rows past M (or N) re-read the last valid
+// row; their outputs are not stored.  Requires K and the K chunk to be multiples of 64.
+namespace {
+constexpr int kSkStages = 4;
+constexpr int kSkStageBytes = 2 * 64 * 128;           // X tile + W tile
+
+__device__ __forceinline__ void sk_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t sk_lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+template <int n>
+__device__ __forceinline__ void sk_wait_vm() {
+  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF));
+}
+__device__ __forceinline__ void sk_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+}  // namespace
+
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(
+    int M, int N, int K, int kchunk, const uint16_t* __restrict__ X, long lda, long sx,
+    const uint16_t* __restrict__ W, long ldw, long sw, typename StoreT<OUT>::type* __restrict__ Y,
+    long ldc, long sy, long ssplit, float alpha, int nsplit) {
+  __shared__ __attribute__((aligned(1024))) char ring[kSkStages * kSkStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int b = blockIdx.z / nsplit, sp = blockIdx.z % nsplit;
+  X += b * sx;
+  W += b * sw;
+  Y += b * sy + sp * ssplit;
+  const int k0 = sp * kchunk;
+  const int nk = (min(K, k0 + kchunk) - k0) / 64;      // 64-wide K steps of this split
+  const int n0 = blockIdx.x * 64;
+
+  // Direct loads: wave w brings rows [16w, 16w + 16) of the X tile and of the W tile, two
+  // 1 KiB instructions each (8 rows x 128 bytes; lane i -> row + (i >> 3), stored chunk i & 7).
+  uint32_t xoff[2], woff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * wave + 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    xoff[q] = uint32_t((long(min(r, M - 1)) * lda + 8 * c) * 2);
+    woff[q] = uint32_t((long(min(n0 + r, N - 1)) * ldw + 8 * c) * 2);
+  }
+  auto issue = [&](int j) {
+    if (j >= nk) return;
+    char* st = ring + (j % kSkStages) * kSkStageBytes;
+    const long kb = long(k0 + 64 * j) * 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      sk_dma16(reinterpret_cast<const char*>(X) + kb, xoff[q], sk_lds_addr(st + (16 * wave + 8 * q) * 128));
+      sk_dma16(reinterpret_cast<const char*>(W) + kb, woff[q], sk_lds_addr(st + 8192 + (16 * wave + 8 * q) * 128));
+    }
+  };
+  auto wait_for = [&](int j) {                          // stage j landed (this wave's part)
+    const int ahead = min(nk - 1, j + kSkStages - 2) - j;
+    if (ahead >= 2) sk_wait_vm<8>();
+    else if (ahead == 1) sk_wait_vm<4>();
+    else sk_wait_vm<0>();
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // operand rows and their chunk XOR
+  int arow[2], brow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    arow[i] = 32 * wm + 16 * i + (lane & 15);
+    brow[i] = 32 * wn + 16 * i + (lane & 15);
+  }
+  const int g = lane >> 4;
+
+#pragma unroll
+  for (int j = 0; j < kSkStages - 1; ++j) issue(j);
+  for (int i = 0; i < nk; ++i) {
+    wait_for(i);
+    sk_barrier();                                       // stage i visible; stage i - 1 consumed
+    issue(i + kSkStages - 1);
+    const char* st = ring + (i % kSkStages) * kSkStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t af[2], bf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        af[t] = *reinterpret_cast<const bf16x8_t*>(st + arow[t] * 128 + 16 * ((4 * kk + g) ^ ((arow[t] >> 1) & 7)));
+        bf[t] = *reinterpret_cast<const bf16x8_t*>(st + 8192 + brow[t] * 128 +
+                                                   16 * ((4 * kk + g) ^ ((brow[t] >> 1) & 7)));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
+    }
+  }
+  // C layout: lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile.
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int gn = n0 + 32 * wn + 16 * c + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gm = 32 * wm + 16 * a + 4 * (lane >> 4) + r;
+        if (gm < M && gn < N) sts_<OUT>(Y, long(gm) * ldc + gn, alpha * acc[a][c][r]);
+      }
+    }
+}
+
+
+// ------------------------------------------------------------------ merge + W_UV (decode)
+// out[b][h][n] = sum_c W_UV^h[n][c] * Otilde[b][h][c] for one head per work-group, where Otilde
+// is the log-sum-exp merge of the attention's split partials, formed on the fly:
+//   m = max_j m_j,  w_j = 2^(m_j - m) / sum_j' 2^(m_j' - m) l_j',  Otilde = sum_j w_j O_j
+// (scores are in base 2).  Otilde is fp32; it enters the bf16 MFMA as a hi + lo pair
+// (hi = bf16(v), lo = bf16(v - hi)), so the product sees it to ~2^-16 relative.  W_UV^h is rows
+// [h (dn + dv) + dn, +dv) of kv_b_proj ([n][c], c contiguous).
+// A work-group serves 32 batch rows of one head with 4 waves: wave w takes rows 16 (w & 1) ..
+// +15 and half of the c range (w >> 1); the two halves' sums meet in LDS.  Each wave merges the
+// partials of its own rows and c range, so every partial is read once.
+template <int NT, int OUT>
+__global__ __launch_bounds__(256) void merge_uv_kernel(
+    int B, int H, int dc, int dn, int splits, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
+  constexpr int dv = 16 * NT;
+  __shared__ f32x4_t red[2][NT][64];                // second c-half sums, [row group][tile][lane]
+  extern __shared__ float wts[];                    // [32 rows][splits]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave & 1, kh = wave >> 1;
+  const int h = blockIdx.x, b0 = blockIdx.y * 32;
+  if (tid < 32) {
+    const int b = b0 + tid;
+    float* w = wts + tid * splits;
+    if (b < B) {
+      const float* ml = part_ml + (long(b) * splits * H + h) * 2;
+      const long step = long(H) * 2;
+      float m = -INFINITY;
+      for (int j = 0; j < splits; ++j) m = fmaxf(m, ml[j * step]);
+      float l = 0.f;
+      for (int j = 0; j < splits; ++j) {
+        const float mj = ml[j * step];
+        const float e = mj == -INFINITY ? 0.f : exp2f(mj - m);
+        w[j] = e;
+        l += e * ml[j * step + 1];
+      }
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      for (int j = 0; j < splits; ++j) w[j] *= inv;
+    } else {
+      for (int j = 0; j < splits; ++j) w[j] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  const int r = 16 * rg + (lane & 15), b = b0 + r, kq = 8 * (lane >> 4);
+  const int half = dc / 2, kbeg = kh * half;
+  const float* wr = wts + r * splits;
+  const float* po = part_o + (long(b < B ? b : 0) * splits * H + h) * dc + kbeg + kq;
+  const long pstride = long(H) * dc;                // between the splits of one (b, h)
+  const uint16_t* wuv = kv_b + (long(h) * (dn + dv) + dn + (lane & 15)) * dc + kbeg + kq;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = 0; k < half; k += 32) {
+    bf16x8_t wf[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) wf[t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * dc + k);
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (b < B) {
+      for (int j = 0; j < splits; ++j) {
+        const float wj = wr[j];
+        const float4 x0 = *reinterpret_cast<const float4*>(po + j * pstride + k);
+        const float4 x1 = *reinterpret_cast<const float4*>(po + j * pstride + k + 4);
+        v[0] += wj * x0.x; v[1] += wj * x0.y; v[2] += wj * x0.z; v[3] += wj * x0.w;
+        v[4] += wj * x1.x; v[5] += wj * x1.y; v[6] += wj * x1.z; v[7] += wj * x1.w;
+      }
+    }
+    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+    bf16x8v hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = (__bf16)v[e];                          // round to nearest even
+      lo[e] = (__bf16)(v[e] - (float)hi[e]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[t], acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[t], acc[t], 0, 0, 0);
+    }
+  }
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[rg][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  // C layout: lane holds C[4 (lane / 16) + i][lane % 16] of each 16 x 16 tile.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const f32x4_t o = acc[t] + red[rg][t][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bo = b0 + 16 * rg + 4 * (lane >> 4) + i;
+      if (bo < B) sts_<OUT>(out, (long(bo) * H + h) * dv + 16 * t + (lane & 15), o[i]);
+    }
+  }
+}
+
+bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
+                            const float* part_ml, const void* kv_b, void* out, hipStream_t st) {
+  if (dv != 128 || dc % 64 != 0 || splits > 256) return false;
+  dim3 grid(H, (B + 31) / 32);
+  const size_t sh = size_t(32) * splits * sizeof(float);
+  if (out_type == K_BF16)
+    hipLaunchKernelGGL((merge_uv_kernel<8, S_BF16>), grid, dim3(256), sh, st, B, H, dc, dn, splits, part_o, part_ml,
+                       static_cast<const uint16_t*>(kv_b), static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL((merge_uv_kernel<8, S_F32>), grid, dim3(256), sh, st, B, H, dc, dn, splits, part_o, part_ml,
+                       static_cast<const uint16_t*>(kv_b), static_cast<float*>(out));
+  return true;
+}
+
 // ------------------------------------------------------------------ launcher
 template <int BM, int BN, int BK, bool NN, int OUT>
 static void launch_bf16(const GemmArgs& g, hipStream_t st) {
@@ -187,6 +424,14 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
 template <bool NN, int OUT>
 static void launch_bf16_shape(const GemmArgs& g, hipStream_t st) {
   long tiles_big = long((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch * g.nsplit;
+  if (!NN && g.M <= 64 && g.kwrap == 0 && g.K % 64 == 0 && g.kchunk % 64 == 0 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
+      long(g.M) * g.lda * 2 < (1L << 32) && long(g.N) * g.ldw * 2 < (1L << 32)) {
+    dim3 grid((g.N + 63) / 64, 1, g.batch * g.nsplit);
+    hipLaunchKernelGGL(gemm_skinny_kernel<OUT>, grid, dim3(256), 0, st, g.M, g.N, g.K, g.kchunk,
+                       static_cast<const uint16_t*>(g.X), g.lda, g.sx, static_cast<const uint16_t*>(g.W), g.ldw, g.sw,
+                       static_cast<typename StoreT<OUT>::type*>(g.Y), g.ldc, g.sy, g.ssplit, g.alpha, g.nsplit);
+    return;
+  }
   if (g.M <= 64)
     launch_bf16<64, 128, 64, NN, OUT>(g, st);
   else if (tiles_big >= 256)

@@ -188,9 +188,13 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   if (ev_attn_end) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_end), s);
 
   void* otilde = at(workspace, p.off_otilde);
+  // out[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  The bf16 path
+  // merges the split partials inside the projection kernel.
+  if (path == PATH_BF16 && launch_decode_merge_uv(kdt(cfg->out_dtype), B, d.H, d.dc, d.dn, d.dv, p.splits,
+                                                  a.part_o, a.part_ml, w->kv_b_proj, out, s))
+    return finish();
   launch_decode_merge(act, B, d.H, d.dc, p.splits, a.part_o, a.part_ml, otilde, s);
-  // out[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  On the bf16 path
-  // otilde is [hi | lo] (2 dc wide) and both halves are multiplied by the same weight row.
+  // On the bf16 path otilde is [hi | lo] (2 dc wide) and both halves meet the same weight row.
   const char* w_uv = static_cast<const char*>(w->kv_b_proj) + size_t(d.dn) * d.dc * asz;
   const int kx = path == PATH_F32 ? d.dc : 2 * d.dc;
   launch_gemm(gemm(path, false, kdt(cfg->out_dtype), B, d.dv, kx, whole(kx), d.H, otilde, long(d.H) * kx, kx,

@@ -70,6 +70,10 @@ bool launch_decode_attn_v2(const DecodeAttnArgs& a, hipStream_t st);
 
 // Log-sum-exp merge of split partials, normalised.  fp32 path: otilde [B][H][dc] fp32; bf16
 // path: otilde [B][H][2*dc] = [hi | lo] with hi = bf16(v), lo = bf16(v - hi).
+// Merge of the split partials fused with the W_UV projection (bf16 path, dv = 128):
+// out[b][h] = W_UV^h Otilde[b][h], out fp32 or bf16 per out_type; false if the shape does not apply.
+bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
+                            const float* part_ml, const void* kv_b, void* out, hipStream_t st);
 void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
                          const float* part_ml, void* otilde, hipStream_t st);
 

@@ -69,7 +69,7 @@ SplitK gemm_splitk(long M, long N, long K, int tile_m, int tile_n) {
   long most = K / 256;
   long n = want < most ? want : most;
   if (n <= 1) return s;
-  long chunk = rup(cdiv(K, n), 32);
+  long chunk = rup(cdiv(K, n), 64);
   s.n = int(cdiv(K, chunk));
   s.chunk = int(chunk);
   return s;
