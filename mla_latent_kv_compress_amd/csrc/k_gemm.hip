@@ -358,6 +358,7 @@ __global__ __launch_bounds__(256) void merge_uv_kernel(
     for (int t = 0; t < NT; ++t) wf[t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * dc + k);
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (b < B) {
+#pragma unroll 4
       for (int j = 0; j < splits; ++j) {
         const float wj = wr[j];
         const float4 x0 = *reinterpret_cast<const float4*>(po + j * pstride + k);
@@ -410,6 +411,104 @@ bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, 
                        static_cast<const uint16_t*>(kv_b), static_cast<float*>(out));
   return true;
 }
+
+// ------------------------------------------------------------------ absorb + query RoPE (decode)
+// qhat[b][h] = [ W_UK^h^T bf16(scale q_nope[b][h]) | bf16(scale RoPE(q_pe[b][h])) ] from the fp32
+// query projection (K-split partials summed in order).  W_UK^h is rows [h (dn + dv), +dn) of
+// kv_b_proj ([d][c], c contiguous): a work-group stages a [dn x 64] column block of it in LDS and
+// reads it with the transposing ds_read_b64_tr_b16 as the B operand (8 consecutive d per lane);
+// the A operand (64 decode rows x 32 d) comes straight from the fp32 projection.  The extra
+// column block blockIdx.x = dc / 64 applies RoPE to q_pe with the token angles in rope_tab.
+template <int DN>
+__global__ __launch_bounds__(256) void absorb_rope_kernel(
+    int B, int H, int dr, int dc, int dv, int nsplit, const float* __restrict__ q_acc,
+    const float* __restrict__ rope_tab, float scale, const uint16_t* __restrict__ kv_b,
+    uint16_t* __restrict__ qhat) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[DN * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.y, b0 = blockIdx.z * 64;
+  const int dqk = DN + dr;
+  const long nq = long(H) * dqk, sstride = long(B) * nq;
+  const float* qh = q_acc + long(h) * dqk;
+  auto qsum = [&](int b, int i) {
+    float v = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) v += qh[sp * sstride + long(b) * nq + i];
+    return v;
+  };
+  if (blockIdx.x * 64 >= dc) {                        // RoPE block
+    const int half = dr / 2;
+    for (int e = tid; e < 64 * half; e += 256) {
+      const int b = b0 + e / half, pi = e % half;
+      if (b >= B) continue;
+      const float c = rope_tab[long(b) * dr + pi], sn = rope_tab[long(b) * dr + half + pi];
+      const float ev = qsum(b, DN + 2 * pi), ov = qsum(b, DN + 2 * pi + 1);
+      uint16_t* o = qhat + (long(b) * H + h) * (dc + dr) + dc + 2 * pi;
+      o[0] = f2bf(scale * (ev * c - ov * sn));
+      o[1] = f2bf(scale * (ev * sn + ov * c));
+    }
+    return;
+  }
+  const int c0 = blockIdx.x * 64;
+  {
+    const uint16_t* wsrc = kv_b + long(h) * (DN + dv) * dc + c0;
+    for (int k = tid; k < DN * 8; k += 256) {
+      const int row = k >> 3, cc = k & 7;
+      *reinterpret_cast<uint4*>(&wt[row * 64 + 8 * cc]) =
+          *reinterpret_cast<const uint4*>(wsrc + long(row) * dc + 8 * cc);
+    }
+  }
+  __syncthreads();
+  const int li = lane & 15, g = lane >> 4;
+  const int b = b0 + 16 * wave + li;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DN / 32; ++ks) {
+    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (b < B) {
+      const float* src = qh + long(b) * nq + 32 * ks + 8 * g;
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float4 x0 = *reinterpret_cast<const float4*>(src + sp * sstride);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + sp * sstride + 4);
+        v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+        v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+      }
+    }
+    bf16x8v a;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = (__bf16)(scale * v[j]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      typedef short s16x4v __attribute__((ext_vector_type(4)));
+      const uint16_t* p0 = &wt[(32 * ks + 8 * g + (li >> 2)) * 64 + 16 * t + 4 * (li & 3)];
+      const s16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p0));
+      const s16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p0 + 4 * 64));
+      typedef short s16x8v __attribute__((ext_vector_type(8)));
+      const s16x8v bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[t], 0, 0, 0);
+    }
+  }
+  // C layout: lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile.
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int bo = b0 + 16 * wave + 4 * g + r;
+      if (bo < B) qhat[(long(bo) * H + h) * (dc + dr) + c0 + 16 * t + li] = f2bf(acc[t][r]);
+    }
+}
+
+bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit, const float* q_acc,
+                        const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st) {
+  if (dn != 128 || dc % 64 != 0 || dr % 2 != 0 || B <= 0) return false;
+  dim3 grid(dc / 64 + 1, H, (B + 63) / 64);
+  hipLaunchKernelGGL(absorb_rope_kernel<128>, grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, q_acc, rope_tab,
+                     scale, static_cast<const uint16_t*>(kv_b), static_cast<uint16_t*>(qhat));
+  return true;
+}
+
 
 // ------------------------------------------------------------------ launcher
 template <int BM, int BN, int BK, bool NN, int OUT>

@@ -21,6 +21,26 @@ __device__ __forceinline__ float split_sum(const float* __restrict__ acc, int n,
   return v;
 }
 
+// Same for four consecutive values i .. i+3 (i and stride multiples of 4, acc 16-byte aligned).
+__device__ __forceinline__ float4 split_sum4(const float* __restrict__ acc, int n, long stride, long i) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  int s = 0;
+  for (; s + 4 <= n; s += 4) {
+    float4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const float4*>(acc + (s + j) * stride + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v.x += x[j].x; v.y += x[j].y; v.z += x[j].z; v.w += x[j].w;
+    }
+  }
+  for (; s < n; ++s) {
+    const float4 x = *reinterpret_cast<const float4*>(acc + s * stride + i);
+    v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+  }
+  return v;
+}
+
 // ------------------------------------------------------------------ compress epilogue
 // One block per token.  a = sum of the kv_a partials = [latent (dc) | k_pe (dr)].
 // latent <- latent / sqrt(mean(latent^2) + eps) * gamma;  k_pe <- RoPE(k_pe, pos);
@@ -29,20 +49,39 @@ template <typename ActT, int CACHE>
 __global__ __launch_bounds__(256) void compress_rows_kernel(
     int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
     const int32_t* __restrict__ pos, const int64_t* __restrict__ slots, void* __restrict__ cache,
-    float* __restrict__ cache_scale, long num_slots, float eps, float theta) {
+    float* __restrict__ cache_scale, long num_slots, float eps, float theta, float* __restrict__ rope_tab,
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks) {
   extern __shared__ float row[];                    // [dc + dr]
   __shared__ float red[16];
   const int t = blockIdx.x, W = dc + dr;
-  const long slot = slots[t];
+  // Decode (ctx given): the token is the last of a context of ctx[t] rows, at position ctx[t] - 1.
+  int p;
+  long slot;
+  if (ctx) {
+    p = ctx[t] - 1;
+    const int page = p >= 0 ? p / kPage : -1;
+    slot = (page >= 0 && page < max_blocks) ? long(bt[long(t) * max_blocks + page]) * kPage + p % kPage : -1;
+    if (p < 0) p = 0;
+  } else {
+    p = pos[t];
+    slot = slots[t];
+  }
+  if (rope_tab)                                     // the token's angles, for its query's RoPE too
+    for (int i = threadIdx.x; i < dr / 2; i += blockDim.x)
+      rope_cs(p, i, dr, theta, &rope_tab[long(t) * dr + i], &rope_tab[long(t) * dr + dr / 2 + i]);
   if (slot < 0 || slot >= num_slots) return;        // uniform over the block
-  for (int i = threadIdx.x; i < W; i += blockDim.x) row[i] = split_sum(acc, nsplit, long(T) * W, long(t) * W + i);
+  if (W % 4 == 0) {
+    for (int i = 4 * threadIdx.x; i < W; i += 4 * blockDim.x)
+      *reinterpret_cast<float4*>(&row[i]) = split_sum4(acc, nsplit, long(T) * W, long(t) * W + i);
+  } else {
+    for (int i = threadIdx.x; i < W; i += blockDim.x) row[i] = split_sum(acc, nsplit, long(T) * W, long(t) * W + i);
+  }
   __syncthreads();
   float ss = 0.f;
   for (int i = threadIdx.x; i < dc; i += blockDim.x) ss += row[i] * row[i];
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / float(dc) + eps);
   for (int i = threadIdx.x; i < dc; i += blockDim.x) row[i] = row[i] * r * ldf<ActT>(gamma, i);
-  const int p = pos[t];
   for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) {
     float c, s;
     rope_cs(p, i, dr, theta, &c, &s);
@@ -71,13 +110,14 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
 void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit, const float* acc,
                           const void* gamma, const int32_t* pos, const int64_t* slots,
                           void* cache_data, float* cache_scale, long num_slots, float eps,
-                          float theta, hipStream_t st) {
+                          float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                          hipStream_t st) {
   if (T <= 0) return;
   size_t sh = size_t(dc + dr) * sizeof(float);
 #define MLA_CR(A, C)                                                                          \
   hipLaunchKernelGGL((compress_rows_kernel<A, C>), dim3(T), dim3(256), sh, st, dc, dr, T, nsplit, \
                      acc, static_cast<const A*>(gamma), pos, slots, cache_data, cache_scale,      \
-                     num_slots, eps, theta)
+                     num_slots, eps, theta, rope_tab, ctx, bt, max_blocks)
   if (act == K_F32) {
     MLA_CR(float, K_F32);
   } else if (cache == K_BF16) {
@@ -98,10 +138,18 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsp
   __shared__ float red[16];
   const int t = blockIdx.x;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const float v = split_sum(acc, nsplit, long(T) * n, long(t) * n + i);
-    row[i] = v;
-    ss += v * v;
+  if (n % 4 == 0) {
+    for (int i = 4 * threadIdx.x; i < n; i += 4 * blockDim.x) {
+      const float4 v = split_sum4(acc, nsplit, long(T) * n, long(t) * n + i);
+      *reinterpret_cast<float4*>(&row[i]) = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+  } else {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const float v = split_sum(acc, nsplit, long(T) * n, long(t) * n + i);
+      row[i] = v;
+      ss += v * v;
+    }
   }
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / float(n) + eps);

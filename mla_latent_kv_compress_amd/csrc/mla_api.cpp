@@ -42,13 +42,14 @@ SplitK whole(int K) { return SplitK{1, (K + 31) / 32 * 32}; }
 void enqueue_compress(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
                       const void* hidden, const int32_t* pos, const int64_t* slots,
                       const mla_cache* cache, int T, const CompressPlan& cp, void* ws,
-                      hipStream_t s) {
+                      hipStream_t s, float* rope_tab = nullptr, const int32_t* ctx = nullptr,
+                      const int32_t* bt = nullptr, int max_blocks = 0) {
   float* acc = reinterpret_cast<float*>(at(ws, cp.off_acc));
   launch_gemm(gemm(path, false, K_F32, T, d.W(), d.D, cp.split, 1, hidden, d.D, 0, w->kv_a_proj, d.D, 0,
                    acc, d.W(), 0), s);
   launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), T, d.dc, d.dr, cp.split.n, acc,
                        w->kv_a_norm, pos, slots, cache->data, cache->scale,
-                       long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.theta, s);
+                       long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.theta, rope_tab, ctx, bt, max_blocks, s);
 }
 
 // Query projection of T tokens.  Leaves fp32 partials at q.off_q_acc, or (q.direct) the scaled
@@ -160,20 +161,32 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   int32_t* pos = reinterpret_cast<int32_t*>(at(workspace, p.off_pos));
   int64_t* slot = reinterpret_cast<int64_t*>(at(workspace, p.off_slot));
 
-  launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
-  enqueue_compress(d, path, cfg, w, hidden, pos, slot, cache, B, p.comp, workspace, s);
+  float* rope = reinterpret_cast<float*>(at(workspace, p.off_rope));
+  if (path == PATH_BF16) {
+    // the row epilogue takes each token's position and slot from its context length itself
+    enqueue_compress(d, path, cfg, w, hidden, nullptr, nullptr, cache, B, p.comp, workspace, s, rope, context_lens,
+                     block_table, max_blocks);
+  } else {
+    launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
+    enqueue_compress(d, path, cfg, w, hidden, pos, slot, cache, B, p.comp, workspace, s, rope);
+  }
   enqueue_query(d, path, cfg, w, hidden, B, p.q, workspace, nullptr, 0.f, s);
 
   // Scaled queries: sigma * log2(e) folded in, so the kernels use exp2.
   const float qscale = d.sigma * kLog2eHost;
   void* qnope = at(workspace, p.off_qnope);
   void* qhat = at(workspace, p.off_qhat);
-  launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n,
-                reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)), pos, qscale, d.theta, qnope, qhat,
-                nullptr, s);
-  // Absorb: qhat[b][h][0:dc] = q_nope[b][h] . W_UK^h  (W_UK^h = kv_b_proj rows of head h's k_nope).
-  launch_gemm(gemm(path, true, act, B, d.dc, d.dn, whole(d.dn), d.H, qnope, long(d.H) * d.dn, d.dn,
-                   w->kv_b_proj, d.dc, long(d.dkv()) * d.dc, qhat, long(d.H) * d.W(), d.W()), s);
+  const float* qacc = reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc));
+  // Absorb: qhat[b][h][0:dc] = q_nope[b][h] . W_UK^h  (W_UK^h = kv_b_proj rows of head h's k_nope),
+  // qhat[b][h][dc:] = RoPE(q_pe[b][h]); one kernel on the bf16 path.
+  if (!(path == PATH_BF16 && launch_absorb_rope(B, d.H, d.dn, d.dr, d.dc, d.dv, p.q.split_b.n, qacc, rope, qscale,
+                                                w->kv_b_proj, qhat, s))) {
+    if (path == PATH_BF16) launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
+    launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n, qacc, pos, qscale, d.theta, qnope, qhat,
+                  nullptr, s);
+    launch_gemm(gemm(path, true, act, B, d.dc, d.dn, whole(d.dn), d.H, qnope, long(d.H) * d.dn, d.dn,
+                     w->kv_b_proj, d.dc, long(d.dkv()) * d.dc, qhat, long(d.H) * d.W(), d.W()), s);
+  }
 
   DecodeAttnArgs a;
   a.B = B; a.H = d.H; a.dc = d.dc; a.dr = d.dr; a.splits = p.splits;

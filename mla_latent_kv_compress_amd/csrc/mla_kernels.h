@@ -31,7 +31,13 @@ enum { K_F32 = 0, K_BF16 = 1, K_FP8 = 2, K_F16 = 3 };
 void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit, const float* acc,
                           const void* gamma, const int32_t* pos, const int64_t* slots,
                           void* cache_data, float* cache_scale, long num_slots, float eps,
-                          float theta, hipStream_t st);
+                          float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                          hipStream_t st);
+// Decode queries on the bf16 path, from the fp32 query projection q ([nsplit][B][H][dn + dr]):
+// qhat[b][h] = [ W_UK^h^T bf16(scale q_nope) | bf16(scale RoPE(q_pe)) ] (bf16), with the
+// angles of each token from rope_tab ([B][dr]: cos | sin).  False if the shape does not apply.
+bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit, const float* q_acc,
+                        const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st);
 
 // out[t][:] = RMSNorm(sum_s acc[s][t][:]) * gamma, in act dtype.
 void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,

@@ -70,6 +70,7 @@ struct DecodePlan {
   size_t off_pos;             // int32 [B]
   size_t off_slot;            // int64 [B]
   size_t off_qnope;           // act  [B][H][dn]   scaled q_nope
+  size_t off_rope;            // fp32 [B][dr]      RoPE angles of the decode tokens (cos | sin)
   size_t off_qhat;            // act  [B][H][W]    absorbed, scaled query
   size_t off_part_o;          // fp32 [B][splits][H][dc]
   size_t off_part_ml;         // fp32 [B][splits][H][2]
