@@ -1,20 +1,24 @@
-// Split-K decode attention over a bf16 latent cache, 128 heads per work-group (weight-absorbed).
+// Split-K decode attention over a bf16 latent cache, 64 heads per work-group (weight-absorbed).
 //
-// One work-group of 4 waves (one per SIMD) per (sequence, split, 128 heads).  The split's
-// cached rows stream through LDS in stages of 32 tokens (32 rows x 576 bf16 = 36 KiB), fetched
-// with direct global->LDS loads into a ring of 4 stages, three stages ahead of the one being
-// computed.  Per stage:
-//   scores    wave w owns heads [32w, 32w+32): S[token][head] = R . Qhat^T with
-//             v_mfma_f32_16x16x32_bf16 (2 token tiles x 2 head tiles, 18 K steps), the query
-//             slice held in registers for the whole split; online softmax per head in base 2
-//             (log2 e is folded into Qhat) with a lazy reference max; P goes to LDS as bf16.
-//   values    wave w owns latent columns [128w, 128w+128) for all 128 heads:
-//             O^T[c][head] += R^T . P^T with v_mfma_f32_32x32x16_bf16 (4 column tiles x 4 head
-//             tiles, 2 K steps of 16 tokens), R^T read with the transposing ds_read_b64_tr_b16.
-// The cached latent is also the value, so one LDS stage feeds both products and each cache row
-// leaves HBM once per split.  Splitting the value product by columns means every wave reads
-// only its quarter of the stage for it (instead of all of it), and the score product's operand
-// is shared by 32 heads per read.
+// One work-group of 8 waves per (sequence, split, group of 64 heads), two waves per SIMD with
+// separate roles:
+//   score waves 0-3   wave w owns heads [16w, 16w+16) of the group: S[token][head] = R . Qhat^T
+//                     with v_mfma_f32_16x16x32_bf16 (2 token tiles, 18 K steps over two
+//                     accumulators per tile), the query slice in registers for the whole split;
+//                     online softmax per head in base 2 (log2 e is folded into Qhat); P to LDS.
+//   value waves 4-7   wave 4+w owns latent columns [128w, 128w+128) for the 64 heads:
+//                     O^T[c][head] += R^T . P^T with v_mfma_f32_32x32x16_bf16 (4 column tiles x
+//                     2 head tiles, 2 K steps of 16 tokens), R^T read with ds_read_b64_tr_b16;
+//                     they also issue the direct global->LDS loads of the cache rows.
+// The split's rows stream through LDS in stages of 32 tokens (32 rows x 576 bf16 = 36 KiB) in a
+// ring of 4, three stages ahead.  Step i runs the value product of stage i next to the score
+// product of stage i + 1 (on different waves of each SIMD, so the matrix core and LDS work of
+// the two overlap), with one work-group barrier per step.  The cached latent is also the value,
+// so one LDS stage feeds both products.  The work-groups of the head groups of one (sequence,
+// split) are dealt to the same XCD next to each other, so they stream the same rows together
+// and the second read of every row is an L2 hit: the cache leaves HBM once per split.  Per SIMD
+// the query slice (72 registers), the fp32 accumulators (128) and the operand prefetch fit the
+// register file of two waves with room to spare.
 //
 // LDS: a stage holds rows of 72 16-byte chunks, unpadded (each direct load instruction fills a
 // contiguous KiB), with chunk c of row r stored at c ^ rsw(r), rsw(r) < 8 (the XOR stays inside
@@ -23,9 +27,7 @@
 // instruction) run at the full 128-bit LDS rate, about twice the rate of the unswizzled rows or
 // of some other XOR patterns; the transposing reads run at their own (lower) rate whatever the
 // pattern.  P is stored [head][token] (64 bytes per head) with the chunk index XORed by
-// (head >> 2) & 3, so 16 consecutive heads of one chunk column (the B operand of 16 lanes) are
-// conflict-free.  A 128-float buffer carries each head's rescale factor from the wave that owns
-// its scores to the waves that own its value columns.
+// (head >> 2) & 3.
 //
 // Reference max: each head accumulates p = 2^(s - m) against a reference m fixed after the
 // first stage (that stage's max), so the accumulators are never rescaled inside the loop.  Later
@@ -50,13 +52,14 @@ constexpr int kPageBytes = kPage * kRowBytes;         // 73728
 constexpr int kStage = 32;                            // tokens per pipeline stage
 constexpr int kStageBytes = kStage * kRowBytes;       // 36864
 constexpr int kRing = 4;
-constexpr int kThreads = 256;
-constexpr int kLoads = kStageBytes / 16 / kThreads;   // 9 direct loads per thread per stage
+constexpr int kThreads = 512;                         // 4 score waves + 4 value waves
+constexpr int kLoads = kStageBytes / 16 / 256;        // 9 direct loads per value-wave thread per stage
 constexpr int kKS = kDW / 32;                         // 18 score K steps
-constexpr int kHeads = 128;                           // heads per work-group
-constexpr int kPBytes = kHeads * kStage * 2;          // 8192
+constexpr int kHeads = 64;                            // heads per work-group
+constexpr int kPBytes = kHeads * kStage * 2;          // 4096
 constexpr float kSlack = 64.0f;
 constexpr int kChecked = 0, kMaxOnly = 1, kFixed = 2;     // pass kinds
+constexpr int kScoreRing = 5;                         // score operand fragments in flight + 1
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -78,6 +81,22 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t v = {(__bf16)a, (__bf16)b};                 // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per 16-lane row) with the gfx950
+// row-swap instructions (VALU, no LDS round trip): permlane16_swap(x, x) returns rows (0,0,2,2)
+// and (1,1,3,3) of x, permlane32_swap(x, x) returns rows (0,1,0,1) and (2,3,2,3).
+__device__ __forceinline__ float max_across_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Wait until at most `n` vector-memory operations of this wave are outstanding (n a constant).
@@ -109,22 +128,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 
-// Enqueue the direct loads of one stage: instruction k of wave w fills LDS bytes
-// [(4k + w) KiB, +1 KiB) of the stage; lane i supplies stored chunk (4k + w) * 64 + i, i.e. row
-// r = chunk / 72, logical chunk (chunk % 72) ^ rsw(r).  Rows at or beyond `valid` re-read row
-// valid - 1.  The lane id arrives opaque so the offsets are recomputed per stage (a few integer
-// ops) instead of being hoisted into registers for the whole loop.
-__device__ __forceinline__ void load_stage(char* dst, const char* src, int valid, int wave, int lane) {
-  asm volatile("" : "+v"(lane));
-#pragma unroll
-  for (int k = 0; k < kLoads; ++k) {
-    const int idx = (4 * k + wave) * 64 + lane;
-    const int r = idx / 72, cp = idx - r * 72;
-    const int c = cp ^ rsw(r);
-    const int rs = r < valid ? r : valid - 1;
-    const uint32_t off = uint32_t(rs * kRowBytes + c * 16);
-    dma16(src, off, lds_addr(dst + (4 * k + wave) * 1024));
-  }
+// Offset, within a stage, of the 16 bytes that lane `lane` of direct-load instruction k of wave
+// `wave` fetches: instruction k of wave w fills LDS bytes [(4k + w) KiB, +1 KiB) of the stage;
+// lane i supplies stored chunk (4k + w) * 64 + i, i.e. row r = chunk / 72, logical chunk
+// (chunk % 72) ^ rsw(r).  Rows at or beyond `valid` re-read row valid - 1.
+__device__ __forceinline__ uint32_t stage_offset(int k, int wave, int lane, int valid) {
+  const int idx = (4 * k + wave) * 64 + lane;
+  const int r = idx / 72, cp = idx - r * 72;
+  const int c = cp ^ rsw(r);
+  const int rs = r < valid ? r : valid - 1;
+  return uint32_t(rs * kRowBytes + c * 16);
 }
 
 }  // namespace
@@ -133,28 +146,36 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     int H, int splits, int max_blocks, int xcd_map, const uint16_t* __restrict__ qhat,
     const uint16_t* __restrict__ cache, const int32_t* __restrict__ bt, const int32_t* __restrict__ ctx_lens,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(1024))) char smem[kRing * kStageBytes + 2 * kPBytes];   // 160 KiB
+  __shared__ __attribute__((aligned(1024))) char smem[kRing * kStageBytes + 2 * kPBytes];
   char* const ring = smem;
   char* const pbase = smem + kRing * kStageBytes;          // P of stage j in pbase + (j & 1) * kPBytes
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool scorer = wid < 4;                             // else a value wave
+  const int wave = wid & 3;                                // index within the role
   const int g = lane >> 4, li = lane & 15;
-  // Work-group -> (sequence, split).  With xcd_map the splits of one sequence share an XCD
-  // (work-groups are dealt to the 8 XCDs round-robin), so its query rows are fetched once per L2.
-  int b, sp;
+  // Work-group -> (sequence, split, head group).  Work-groups are dealt to the 8 XCDs
+  // round-robin; with xcd_map the head groups of one (sequence, split) land on the same XCD in
+  // consecutive rounds.
+  const int G = H / kHeads;
+  int b, sp, hg;
   {
     const int unit = blockIdx.x;
     if (xcd_map) {
       const int k = unit >> 3;
-      b = (k / splits) * 8 + (unit & 7);
-      sp = k - (k / splits) * splits;
+      const int k2 = k / G;
+      hg = k - k2 * G;
+      b = (k2 / splits) * 8 + (unit & 7);
+      sp = k2 - (k2 / splits) * splits;
     } else {
-      b = unit / splits;
-      sp = unit - b * splits;
+      hg = unit % G;
+      const int k2 = unit / G;
+      b = k2 / splits;
+      sp = k2 - b * splits;
     }
   }
-  const int hbase = blockIdx.y * kHeads;
+  const int hbase = hg * kHeads;
   const int ctx = ctx_lens[b];
   const int nst = (ctx + kStage - 1) / kStage;
   const int per = (nst + splits - 1) / splits;
@@ -163,11 +184,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   const char* cbase = reinterpret_cast<const char*>(cache);
   const int32_t* btab = bt + long(b) * max_blocks;
   auto stage_valid = [&](int j) { return j < n ? min(kStage, ctx - kStage * (s0 + j)) : 0; };
+
+  // ---- value-wave state: direct loads, transposing reads, accumulators
+  uint32_t full_off[kLoads];             // offsets of a stage whose rows are all cached
+  if (!scorer) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) full_off[k] = stage_offset(k, wave, lane, kStage);
+  }
   auto issue = [&](int j) {              // loads of stage j (of this split) into ring slot j % 4
-    if (j < n)
-      load_stage(ring + (j & 3) * kStageBytes,
-                 cbase + long(btab[(s0 + j) >> 1]) * kPageBytes + ((s0 + j) & 1) * kStageBytes, stage_valid(j),
-                 wave, lane);
+    if (j >= n) return;
+    char* dst = ring + (j & 3) * kStageBytes;
+    const char* src = cbase + long(btab[(s0 + j) >> 1]) * kPageBytes + ((s0 + j) & 1) * kStageBytes;
+    const int valid = stage_valid(j);
+    if (valid == kStage) {
+#pragma unroll
+      for (int k = 0; k < kLoads; ++k) dma16(src, full_off[k], lds_addr(dst + (4 * k + wave) * 1024));
+    } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int k = 0; k < kLoads; ++k)
+        dma16(src, stage_offset(k, wave, ln, valid), lds_addr(dst + (4 * k + wave) * 1024));
+    }
   };
   // Wait until stage j is in LDS, stages up to `last` having been issued (in order).
   auto wait_stage = [&](int j, int last) {
@@ -177,23 +215,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     else wait_vm<0>();
   };
 
-  // Query fragments (B operand of the score product): Qhat[head 32w + 16nt + li][32ks + 8g .. +7].
-  bf16x8_t qf[2][kKS];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const uint16_t* q = qhat + (long(b) * H + hbase + 32 * wave + 16 * nt + li) * kDW + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) qf[nt][ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
-  }
-
+  // ---- shared LDS addressing
   // Score operand offsets: row 16 mt + li, logical chunk 4 ks + g, stored at
   // (4 ks + g) ^ rsw(li) = 4 (ks ^ y) + x.
+  // A score wave owns token tile mt_w (tokens [16 mt_w, 16 mt_w + 16) of every stage) and head
+  // half hh (heads [32 hh, 32 hh + 32) of the group); rsw(16 mt_w + li) = rsw(li).
+  const int mt_w = wave & 1, hh = wave >> 1;
   const int sx = g ^ (rsw(li) & 3), sy = rsw(li) >> 2;
-  const int s_even = li * kRowBytes + 16 * sx + 64 * sy;   // ks even: + 64 ks
-  const int s_odd = li * kRowBytes + 16 * sx - 64 * sy;    // ks odd:  + 64 ks
-  auto score_a = [&](const char* st, int ks, int mt) {
-    const int off = ((ks & 1) ? s_odd : s_even) + 64 * ks + mt * 16 * kRowBytes;
-    return *reinterpret_cast<const bf16x8_t*>(st + off);
+  const int s_row = (16 * mt_w + li) * kRowBytes + 16 * sx;
+  const int s_even = s_row + 64 * sy;                      // ks even: + 64 ks
+  const int s_odd = s_row - 64 * sy;                       // ks odd:  + 64 ks
+  auto score_a = [&](const char* st, int ks) {
+    return *reinterpret_cast<const bf16x8_t*>(st + ((ks & 1) ? s_odd : s_even) + 64 * ks);
   };
   // Transposing reads for the value product: lane reads row 8 (lane >> 5) + 4 rd + (li >> 2)
   // (+16 per K step), element column 128 w + 32 ct + 16 ((lane >> 4) & 1) + 4 (li & 3).
@@ -221,215 +254,272 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     return *reinterpret_cast<const bf16x8_t*>(pb + h * 64 + 16 * (c ^ psw(h)));
   };
 
-  f32x16_t o[4][4];
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2];
-  f32x4_t s[2][2];
-
-  // Online softmax of the score tile s against the reference; `valid` tokens of the stage are
-  // cached.  kChecked: the first stage sets the reference; flags scores beyond it + kSlack.
-  auto softmax = [&](auto mode, int valid, uint2 (&pk)[2][2], bool& over) {
-    constexpr int kMode = decltype(mode)::value;
-    const int lim = valid - 4 * g;      // token 16 mt + 4 g + j is cached iff 16 mt + j < lim
+  // ---- score-wave state
+  // Query fragments (B operand of the score product): Qhat[head 32 hh + 16 nt + li][32 ks + 8 g .. +7].
+  bf16x8_t qf[2][kKS];
+  if (scorer) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float mx = -INFINITY;
+      const uint16_t* q = qhat + (long(b) * H + hbase + 32 * hh + 16 * nt + li) * kDW + 8 * g;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int ks = 0; ks < kKS; ++ks) qf[nt][ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
+    }
+  }
+  float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4_t s[2][2];                      // [head tile][K-step parity]
+  f32x16_t o[4][2];
+  // The two score waves of a head half (wave and wave ^ 1) exchange their per-head maxima and
+  // row sums through LDS: xm / lx[head][token tile], in the second P buffer (idle then).
+  float* const xm = reinterpret_cast<float*>(pbase + kPBytes);
+  float* const lx = reinterpret_cast<float*>(pbase + kPBytes + 2 * kHeads * 4);
+  auto hrow = [&](int nt) { return 32 * hh + 16 * nt + li; };
+
+  // Scores of the stage's tile (C layout: lane holds tokens 16 mt_w + 4 g + j, j < 4, of head
+  // hrow(nt)), masked beyond the `valid` cached tokens, and each head's max over the tile.
+  auto mask = [&](int valid, f32x4_t (&v)[2]) {
+    const int lim = valid - 16 * mt_w - 4 * g;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = (16 * mt + j) < lim ? s[mt][nt][j] : -INFINITY;
-          s[mt][nt][j] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (kMode == kMaxOnly) {
-        m_ref[nt] = fmaxf(m_ref[nt], mx);
-        continue;
-      }
-      if (kMode == kChecked) {
-        if (m_ref[nt] == -INFINITY) m_ref[nt] = mx;      // first stage of the split
-        over |= mx > m_ref[nt] + kSlack;
-      }
-      // (an empty split keeps m = -inf; its masked scores then still give p = 0)
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[nt][j] = j < lim ? s[nt][0][j] + s[nt][1][j] : -INFINITY;
+  };
+  auto tile = [&](int valid, f32x4_t (&v)[2], float (&mx)[2]) {
+    mask(valid, v);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      mx[nt] = max_across_rows(fmaxf(fmaxf(v[nt][0], v[nt][1]), fmaxf(v[nt][2], v[nt][3])));
+  };
+  // Whether some score of the tile exceeds its head's reference by more than kSlack.
+  auto beyond = [&](const f32x4_t (&v)[2]) {
+    bool r = false;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r |= v[nt][j] > m_ref[nt] + kSlack;
+    return r;
+  };
+  // p = 2^(s - m) against the reference (an empty split keeps m = -inf and uses 0: its masked
+  // scores still give p = 0), packed to bf16 for the value product; l accumulates the fp32 p.
+  auto weigh = [&](const f32x4_t (&v)[2], uint2 (&pk)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
       const float m_use = m_ref[nt] == -INFINITY ? 0.f : m_ref[nt];
-      float psum = 0.f;
+      float p[4], psum = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(s[mt][nt][j] - m_use);       // 0 for masked tokens
-          psum += p[j];
-        }
-        pk[mt][nt] = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(v[nt][j] - m_use);   // 0 for masked tokens
+        psum += p[j];
       }
+      pk[nt] = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
       l_run[nt] += psum;
     }
   };
-  auto store_p = [&](char* pb, const uint2 (&pk)[2][2]) {
+  auto store_p = [&](char* pb, const uint2 (&pk)[2]) {
+    const int c = 2 * mt_w + (g >> 1);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int h = 32 * wave + 16 * nt + li;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int c = 2 * mt + (g >> 1);
-        *reinterpret_cast<uint2*>(pb + h * 64 + 16 * (c ^ psw(h)) + 8 * (g & 1)) = pk[mt][nt];
-      }
+      const int h = hrow(nt);
+      *reinterpret_cast<uint2*>(pb + h * 64 + 16 * (c ^ psw(h)) + 8 * (g & 1)) = pk[nt];
     }
   };
-  auto zero_s = [&]() {
+  // Score tile of one stage: each K-tile fragment feeds both head tiles; K steps alternate
+  // between two accumulators per head tile (four independent MFMA chains); fragments are read
+  // kScoreRing - 1 K steps ahead of use.
+  auto scores = [&](const char* st) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) s[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
-  // Score tile of one stage, with `extra(ks)` issued after each K step's MFMAs (the value
-  // product of the previous stage rides along so the MFMA pipe stays busy).
-  auto scores = [&](const char* st, auto extra) {
-    zero_s();
-    bf16x8_t a[2][2];
-    a[0][0] = score_a(st, 0, 0);
-    a[0][1] = score_a(st, 0, 1);
+      for (int q = 0; q < 2; ++q) s[nt][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t a[kScoreRing];
+#pragma unroll
+    for (int j = 0; j < kScoreRing - 1; ++j) a[j] = score_a(st, j);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      if (ks + 1 < kKS) {
-        a[(ks + 1) & 1][0] = score_a(st, ks + 1, 0);
-        a[(ks + 1) & 1][1] = score_a(st, ks + 1, 1);
+      const int kn = ks + kScoreRing - 1;
+      if (kn < kKS) a[kn % kScoreRing] = score_a(st, kn);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        s[nt][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks % kScoreRing], qf[nt][ks], s[nt][ks & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);        // keep the source order: reads stay ahead of use
+    }
+  };
+  // Value product of one stage (value waves).
+  auto values = [&](const char* st, const char* pb) {
+    bf16x8_t pf[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) pf[ks][nt] = p_frag(pb, ks, nt);
+    bf16x8_t av[2];
+    av[0] = val_a(st, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {                        // (K step u >> 2, column tile u & 3)
+      if (u + 1 < 8) av[(u + 1) & 1] = val_a(st, (u + 1) >> 2, (u + 1) & 3);
+      const int ks = u >> 2, ct = u & 3;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        o[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u & 1], pf[ks][nt], o[ct][nt], 0, 0, 0);
+    }
+  };
+
+  // The two roles run separate code (so their registers overlap) with the same sequence of
+  // work-group barriers.  Pass structure: an accumulating pass against the first stage's max;
+  // if any score outgrew its reference by kSlack, a scores-only pass for the exact maxima and an
+  // accumulating pass against them.  Stage j's P lives in P buffer j % 2; stage j in ring slot
+  // j % 4.
+  int* flags = reinterpret_cast<int*>(pbase);
+  // Every wave calls this at the end of a pass; score waves also add their partner's row sums.
+  auto restart_needed = [&](bool over, float (&lsum)[2]) {
+    if (scorer) {
+      const bool any_over = __any(over);
+      if (lane == 0) flags[wave] = any_over ? 1 : 0;
+      if (g == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) lx[2 * hrow(nt) + mt_w] = lsum[nt];
       }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks & 1][mt], qf[nt][ks], s[mt][nt], 0, 0, 0);
-      extra(ks);
     }
-  };
-
-  // Scores-only pass over the split: each head's exact max.
-  auto max_pass = [&]() {
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_stage(0, 2);
-    lds_barrier();
-    for (int i = 0; i < n; ++i) {
-      scores(ring + (i & 3) * kStageBytes, [](int) {});
-      uint2 pk[2][2];
-      bool over = false;
-      softmax(std::integral_constant<int, kMaxOnly>(), stage_valid(i), pk, over);
-      lds_barrier();                    // every wave is done with stage i's slot
-      issue(i + 3);
-      wait_stage(i + 1, i + 3);
-      lds_barrier();
-    }
-  };
-
-  // Accumulating pass, software-pipelined: step i computes the value product of stage i
-  // interleaved with the score product of stage i + 1, then the softmax of stage i + 1, with
-  // one barrier per step.  Stage j's P lives in P buffer j % 2; stage j in ring slot j % 4.
-  // Returns true (work-group uniform) if a kChecked pass gave up.
-  auto accumulate = [&](auto mode) -> bool {
-    constexpr int kMode = decltype(mode)::value;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[ct][nt][e] = 0.f;
-    l_run[0] = l_run[1] = 0.f;
-    bool over = false;
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_stage(0, 2);
-    lds_barrier();
-    {
-      uint2 pk[2][2];
-      scores(ring, [](int) {});
-      softmax(mode, stage_valid(0), pk, over);
-      store_p(pbase, pk);
-    }
-    wait_stage(1, 2);
-    lds_barrier();
-    for (int i = 0; i < n; ++i) {
-      issue(i + 3);                     // into the slot of stage i - 1, free since the last barrier
-      const char* st_v = ring + (i & 3) * kStageBytes;
-      const char* pb_v = pbase + (i & 1) * kPBytes;
-      // value product of stage i: unit u = (K step u >> 4, column tile (u >> 2) & 3, head tile u & 3)
-      bf16x8_t pb[4], av[2];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) pb[nt] = p_frag(pb_v, 0, nt);
-      av[0] = val_a(st_v, 0, 0);
-      auto pv_unit = [&](int u) {
-        const int ks = u >> 4, ct = (u >> 2) & 3, nt = u & 3;
-        if (nt == 0 && u + 4 < 32) av[((u >> 2) + 1) & 1] = val_a(st_v, (u + 4) >> 4, ((u + 4) >> 2) & 3);
-        o[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[(u >> 2) & 1], pb[nt], o[ct][nt], 0, 0, 0);
-        if (ks == 0 && ct == 3) pb[nt] = p_frag(pb_v, 1, nt);     // last use of K step 0's fragment
-      };
-      // score product of stage i + 1 (a stage past the split's end scores with every token masked)
-      scores(ring + ((i + 1) & 3) * kStageBytes, [&](int ks) {
-        if (ks < 12) {
-          pv_unit(2 * ks);
-          pv_unit(2 * ks + 1);
-        }
-      });
-      uint2 pk[2][2];
-      softmax(mode, stage_valid(i + 1), pk, over);
-#pragma unroll
-      for (int u = 24; u < 32; ++u) pv_unit(u);
-      store_p(pbase + ((i + 1) & 1) * kPBytes, pk);
-      wait_stage(i + 2, i + 3);
-      lds_barrier();
-    }
-    if (kMode != kChecked) return false;
-    // gave up if any wave saw a score beyond its head's reference + kSlack
-    int* flags = reinterpret_cast<int*>(pbase);
-    const bool any_over = __any(over);
-    if (lane == 0) flags[wave] = any_over ? 1 : 0;
     lds_barrier();
     const int4 f = *reinterpret_cast<const int4*>(flags);
+    if (scorer) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) lsum[nt] += lx[2 * hrow(nt) + (mt_w ^ 1)];
+    }
     lds_barrier();
     return (f.x | f.y | f.z | f.w) != 0;
   };
-
-  if (accumulate(std::integral_constant<int, kChecked>())) {
-    max_pass();
-    accumulate(std::integral_constant<int, kFixed>());
-  }
-
-  // ---- partial state of this split
-  const long row0 = (long(b) * splits + sp) * H + hbase;
+  if (scorer) {
+    // The score waves carry each stage's serial chain (operand reads, products, softmax, P), the
+    // value waves' products fill the matrix core around it: give the score waves issue priority.
+    __builtin_amdgcn_s_setprio(1);
+    // One accumulating pass.  At stage 0 the two waves of a head half agree on the reference:
+    // the stage's max (checked pass) or the maxima the scores-only pass found (fixed pass).
+    auto accumulate = [&](auto mode) {
+      constexpr int kMode = decltype(mode)::value;
+      bool over = false;
+      l_run[0] = l_run[1] = 0.f;
+      lds_barrier();                            // stage 0 loaded
+      {
+        f32x4_t v[2];
+        float mx[2], mine[2];
+        uint2 pk[2];
+        scores(ring);
+        tile(stage_valid(0), v, mx);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float l = l_run[nt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (g == 0) {
-      const long row = row0 + 32 * wave + 16 * nt + li;
-      part_ml[row * 2] = m_ref[nt];
-      part_ml[row * 2 + 1] = l;
+        for (int nt = 0; nt < 2; ++nt) {
+          mine[nt] = kMode == kChecked ? mx[nt] : m_ref[nt];
+          if (g == 0) xm[2 * hrow(nt) + mt_w] = mine[nt];
+        }
+        lds_barrier();                          // maxima exchanged
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) m_ref[nt] = fmaxf(mine[nt], xm[2 * hrow(nt) + (mt_w ^ 1)]);
+        weigh(v, pk);
+        store_p(pbase, pk);
+      }
+      lds_barrier();                            // P(0) published, stage 1 loaded
+      for (int i = 0; i < n; ++i) {
+        if (i + 1 < n) {
+          f32x4_t v[2];
+          uint2 pk[2];
+          scores(ring + ((i + 1) & 3) * kStageBytes);
+          mask(stage_valid(i + 1), v);
+          if (kMode == kChecked) over |= beyond(v);
+          weigh(v, pk);
+          store_p(pbase + ((i + 1) & 1) * kPBytes, pk);
+        }
+        lds_barrier();
+      }
+      return over;
+    };
+    float lsum[2];
+    auto totals = [&]() {
+      lsum[0] = sum_across_rows(l_run[0]);
+      lsum[1] = sum_across_rows(l_run[1]);
+    };
+    const bool over = accumulate(std::integral_constant<int, kChecked>());
+    totals();
+    if (restart_needed(over, lsum)) {
+      m_ref[0] = m_ref[1] = -INFINITY;
+      lds_barrier();                            // stage 0 loaded
+      for (int i = 0; i < n; ++i) {
+        f32x4_t v[2];
+        float mx[2];
+        scores(ring + (i & 3) * kStageBytes);
+        tile(stage_valid(i), v, mx);
+        m_ref[0] = fmaxf(m_ref[0], mx[0]);
+        m_ref[1] = fmaxf(m_ref[1], mx[1]);
+        lds_barrier();
+      }
+      accumulate(std::integral_constant<int, kFixed>());
+      totals();
+      restart_needed(false, lsum);
     }
-  }
+    if (mt_w == 0 && g == 0) {
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    float* dst = part_o + (row0 + 32 * nt + ph) * kDC + 128 * wave + 4 * (lane >> 5);
+      for (int nt = 0; nt < 2; ++nt) {
+        const long row = (long(b) * splits + sp) * H + hbase + hrow(nt);
+        part_ml[row * 2] = m_ref[nt];
+        part_ml[row * 2 + 1] = lsum[nt];
+      }
+    }
+  } else {
+    auto accumulate = [&]() {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4_t*>(dst + 32 * ct + 8 * q) =
-            f32x4_t{o[ct][nt][4 * q], o[ct][nt][4 * q + 1], o[ct][nt][4 * q + 2], o[ct][nt][4 * q + 3]};
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[ct][nt][e] = 0.f;
+      issue(0);
+      issue(1);
+      issue(2);
+      wait_stage(0, 2);
+      lds_barrier();                            // stage 0 loaded
+      lds_barrier();                            // (score waves exchange maxima)
+      wait_stage(1, 2);
+      lds_barrier();
+      for (int i = 0; i < n; ++i) {
+        issue(i + 3);                           // into the slot of stage i - 1, free since the last barrier
+        values(ring + (i & 3) * kStageBytes, pbase + (i & 1) * kPBytes);
+        wait_stage(i + 2, i + 3);
+        lds_barrier();
+      }
+      return false;
+    };
+    float unused[2] = {0.f, 0.f};
+    if (restart_needed(accumulate(), unused)) {
+      issue(0);
+      issue(1);
+      issue(2);
+      wait_stage(0, 2);
+      lds_barrier();
+      for (int i = 0; i < n; ++i) {
+        issue(i + 3);
+        wait_stage(i + 1, i + 3);
+        lds_barrier();
+      }
+      restart_needed(accumulate(), unused);
+    }
+    const long row0 = (long(b) * splits + sp) * H + hbase;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float* dst = part_o + (row0 + 32 * nt + ph) * kDC + 128 * wave + 4 * (lane >> 5);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(dst + 32 * ct + 8 * q) =
+              f32x4_t{o[ct][nt][4 * q], o[ct][nt][4 * q + 1], o[ct][nt][4 * q + 2], o[ct][nt][4 * q + 3]};
+    }
   }
 }
 
 bool launch_decode_attn_v2(const DecodeAttnArgs& a, hipStream_t st) {
   if (a.H % kHeads != 0 || a.dc != kDC || a.dr != kDR) return false;
-  const long units = long(a.B) * a.splits;
+  const long units = long(a.B) * a.splits * (a.H / kHeads);
   const int xcd_map = (a.B % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(decode_attn_latent_kernel, dim3(unsigned(units), a.H / kHeads), dim3(kThreads), 0, st, a.H,
-                     a.splits, a.max_blocks, xcd_map, static_cast<const uint16_t*>(a.qhat),
-                     static_cast<const uint16_t*>(a.cache), a.block_table, a.ctx, a.part_o, a.part_ml);
+  hipLaunchKernelGGL(decode_attn_latent_kernel, dim3(unsigned(units)), dim3(kThreads), 0, st, a.H, a.splits,
+                     a.max_blocks, xcd_map, static_cast<const uint16_t*>(a.qhat), static_cast<const uint16_t*>(a.cache),
+                     a.block_table, a.ctx, a.part_o, a.part_ml);
   return true;
 }
 

@@ -100,7 +100,6 @@ static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q
 
 int decode_heads_per_group(const Dims& d, Path path) {
   if (path != PATH_BF16) return 1;
-  if (d.cache_dt == MLA_BF16 && d.H % 128 == 0) return 128;
   for (int g = 64; g >= 16; g /= 2)
     if (d.H % g == 0) return g;
   return 16;
