@@ -204,22 +204,34 @@ __device__ __forceinline__ void sk_barrier() {
 }
 }  // namespace
 
+// One skinny problem: Y[z / nsplit] (+ split z % nsplit) = alpha X W^T over the split's K chunk.
+struct SkinnyProb {
+  int M, N, K, kchunk, nsplit;
+  const uint16_t* X;
+  long lda, sx;
+  const uint16_t* W;
+  long ldw, sw;
+  void* Y;
+  long ldc, sy, ssplit;
+  float alpha;
+};
+
+// Output tile (64 rows x 64 columns from column tile nx) of batch-and-split index z.
 template <int OUT>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(
-    int M, int N, int K, int kchunk, const uint16_t* __restrict__ X, long lda, long sx,
-    const uint16_t* __restrict__ W, long ldw, long sw, typename StoreT<OUT>::type* __restrict__ Y,
-    long ldc, long sy, long ssplit, float alpha, int nsplit) {
-  __shared__ __attribute__((aligned(1024))) char ring[kSkStages * kSkStageBytes];
+__device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, char* ring) {
+  const int M = p.M, N = p.N, K = p.K, kchunk = p.kchunk, nsplit = p.nsplit;
+  const long lda = p.lda, ldw = p.ldw, ldc = p.ldc;
+  const float alpha = p.alpha;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int b = blockIdx.z / nsplit, sp = blockIdx.z % nsplit;
-  X += b * sx;
-  W += b * sw;
-  Y += b * sy + sp * ssplit;
+  const int b = z / nsplit, sp = z % nsplit;
+  const uint16_t* X = p.X + b * p.sx;
+  const uint16_t* W = p.W + b * p.sw;
+  typename StoreT<OUT>::type* Y = static_cast<typename StoreT<OUT>::type*>(p.Y) + b * p.sy + sp * p.ssplit;
   const int k0 = sp * kchunk;
   const int nk = (min(K, k0 + kchunk) - k0) / 64;      // 64-wide K steps of this split
-  const int n0 = blockIdx.x * 64;
+  const int n0 = nx * 64;
 
   // Direct loads: wave w brings rows [16w, 16w + 16) of the X tile and of the W tile, two
   // 1 KiB instructions each (8 rows x 128 bytes; lane i -> row + (i >> 3), stored chunk i & 7).
@@ -296,6 +308,27 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
         if (gm < M && gn < N) sts_<OUT>(Y, long(gm) * ldc + gn, alpha * acc[a][c][r]);
       }
     }
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyProb p) {
+  __shared__ __attribute__((aligned(1024))) char ring[kSkStages * kSkStageBytes];
+  skinny_tile<OUT>(p, blockIdx.x, blockIdx.z, ring);
+}
+
+// Two independent skinny problems in one launch: work-groups [0, tiles0) take p0's tiles,
+// the rest p1's (one launch instead of two dependent-free ones back to back).
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_skinny_pair_kernel(SkinnyProb p0, SkinnyProb p1, int tiles0) {
+  __shared__ __attribute__((aligned(1024))) char ring[kSkStages * kSkStageBytes];
+  const int id = blockIdx.x;
+  if (id < tiles0) {
+    const int nx = (p0.N + 63) / 64;
+    skinny_tile<OUT>(p0, id % nx, id / nx, ring);
+  } else {
+    const int nx = (p1.N + 63) / 64;
+    skinny_tile<OUT>(p1, (id - tiles0) % nx, (id - tiles0) / nx, ring);
+  }
 }
 
 
@@ -520,15 +553,30 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
                      static_cast<typename StoreT<OUT>::type*>(g.Y), g.ldc, g.sy, g.ssplit, g.alpha, g.nsplit);
 }
 
+// The skinny kernel's conditions: TN, M <= 64, K and the chunk in 64-steps, 16-byte rows, and
+// per-operand offsets that fit the 32-bit load offsets.
+static bool skinny_ok(const GemmArgs& g) {
+  return g.kind == GEMM_BF16 && !g.nn && g.M <= 64 && g.kwrap == 0 && g.K % 64 == 0 && g.kchunk % 64 == 0 &&
+         g.lda % 8 == 0 && g.ldw % 8 == 0 && long(g.M) * g.lda * 2 < (1L << 32) &&
+         long(g.N) * g.ldw * 2 < (1L << 32);
+}
+
+static SkinnyProb skinny_prob(const GemmArgs& g) {
+  SkinnyProb p;
+  p.M = g.M; p.N = g.N; p.K = g.K; p.kchunk = g.kchunk; p.nsplit = g.nsplit;
+  p.X = static_cast<const uint16_t*>(g.X); p.lda = g.lda; p.sx = g.sx;
+  p.W = static_cast<const uint16_t*>(g.W); p.ldw = g.ldw; p.sw = g.sw;
+  p.Y = g.Y; p.ldc = g.ldc; p.sy = g.sy; p.ssplit = g.ssplit;
+  p.alpha = g.alpha;
+  return p;
+}
+
 template <bool NN, int OUT>
 static void launch_bf16_shape(const GemmArgs& g, hipStream_t st) {
   long tiles_big = long((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch * g.nsplit;
-  if (!NN && g.M <= 64 && g.kwrap == 0 && g.K % 64 == 0 && g.kchunk % 64 == 0 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
-      long(g.M) * g.lda * 2 < (1L << 32) && long(g.N) * g.ldw * 2 < (1L << 32)) {
+  if (skinny_ok(g)) {
     dim3 grid((g.N + 63) / 64, 1, g.batch * g.nsplit);
-    hipLaunchKernelGGL(gemm_skinny_kernel<OUT>, grid, dim3(256), 0, st, g.M, g.N, g.K, g.kchunk,
-                       static_cast<const uint16_t*>(g.X), g.lda, g.sx, static_cast<const uint16_t*>(g.W), g.ldw, g.sw,
-                       static_cast<typename StoreT<OUT>::type*>(g.Y), g.ldc, g.sy, g.ssplit, g.alpha, g.nsplit);
+    hipLaunchKernelGGL(gemm_skinny_kernel<OUT>, grid, dim3(256), 0, st, skinny_prob(g));
     return;
   }
   if (g.M <= 64)
@@ -544,6 +592,17 @@ static void launch_bf16_out(const GemmArgs& g, hipStream_t st) {
   if (g.out == K_BF16) launch_bf16_shape<NN, S_BF16>(g, st);
   else if (g.out == K_F16) launch_bf16_shape<NN, S_F16>(g, st);
   else launch_bf16_shape<NN, S_F32>(g, st);
+}
+
+bool launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0 || a.batch <= 0 || b.M <= 0 || b.N <= 0 || b.batch <= 0) return false;
+  if (!skinny_ok(a) || !skinny_ok(b) || a.out != K_F32 || b.out != K_F32) return false;
+  const long t0 = long((a.N + 63) / 64) * a.batch * a.nsplit;
+  const long t1 = long((b.N + 63) / 64) * b.batch * b.nsplit;
+  if (t0 + t1 > (1L << 31) - 1) return false;
+  hipLaunchKernelGGL(gemm_skinny_pair_kernel<S_F32>, dim3(unsigned(t0 + t1)), dim3(256), 0, st, skinny_prob(a),
+                     skinny_prob(b), int(t0));
+  return true;
 }
 
 void launch_gemm(const GemmArgs& g, hipStream_t st) {

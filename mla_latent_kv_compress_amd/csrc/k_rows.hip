@@ -22,21 +22,21 @@ __device__ __forceinline__ float split_sum(const float* __restrict__ acc, int n,
 }
 
 // Same for four consecutive values i .. i+3 (i and stride multiples of 4, acc 16-byte aligned).
+// The loads of up to 8 splits are in flight together, so a row costs one or two memory
+// latencies rather than one per few splits; the adds stay in split order.
 __device__ __forceinline__ float4 split_sum4(const float* __restrict__ acc, int n, long stride, long i) {
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = 0;
-  for (; s + 4 <= n; s += 4) {
-    float4 x[4];
+  for (int s = 0; s < n; s += 8) {
+    float4 x[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const float4*>(acc + (s + j) * stride + i);
+    for (int j = 0; j < 8; ++j)
+      x[j] = s + j < n ? *reinterpret_cast<const float4*>(acc + (s + j) * stride + i) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v.x += x[j].x; v.y += x[j].y; v.z += x[j].z; v.w += x[j].w;
+    for (int j = 0; j < 8; ++j) {
+      if (s + j < n) {
+        v.x += x[j].x; v.y += x[j].y; v.z += x[j].z; v.w += x[j].w;
+      }
     }
-  }
-  for (; s < n; ++s) {
-    const float4 x = *reinterpret_cast<const float4*>(acc + s * stride + i);
-    v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
   }
   return v;
 }
@@ -46,14 +46,12 @@ __device__ __forceinline__ float4 split_sum4(const float* __restrict__ acc, int 
 // latent <- latent / sqrt(mean(latent^2) + eps) * gamma;  k_pe <- RoPE(k_pe, pos);
 // the row is rounded to the cache format and written to its slot (skipped if out of range).
 template <typename ActT, int CACHE>
-__global__ __launch_bounds__(256) void compress_rows_kernel(
-    int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
+__device__ __forceinline__ void compress_row(
+    int t, int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
     const int32_t* __restrict__ pos, const int64_t* __restrict__ slots, void* __restrict__ cache,
     float* __restrict__ cache_scale, long num_slots, float eps, float theta, float* __restrict__ rope_tab,
-    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks) {
-  extern __shared__ float row[];                    // [dc + dr]
-  __shared__ float red[16];
-  const int t = blockIdx.x, W = dc + dr;
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks, float* row, float* red) {
+  const int W = dc + dr;
   // Decode (ctx given): the token is the last of a context of ctx[t] rows, at position ctx[t] - 1.
   int p;
   long slot;
@@ -66,9 +64,18 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
     p = pos[t];
     slot = slots[t];
   }
-  if (rope_tab)                                     // the token's angles, for its query's RoPE too
-    for (int i = threadIdx.x; i < dr / 2; i += blockDim.x)
-      rope_cs(p, i, dr, theta, &rope_tab[long(t) * dr + i], &rope_tab[long(t) * dr + dr / 2 + i]);
+  // The token's RoPE angles, pair ri on the block's last dr / 2 threads (which the split sums
+  // below leave idle when the row is narrow, so the fp64 work overlaps their loads); also written
+  // to rope_tab for the query's RoPE.  dr <= 256 (validated), so dr / 2 <= blockDim.x.
+  const int ri = int(threadIdx.x) - (int(blockDim.x) - dr / 2);
+  float rc = 1.f, rsn = 0.f;
+  if (ri >= 0) {
+    rope_cs(p, ri, dr, theta, &rc, &rsn);
+    if (rope_tab) {
+      rope_tab[long(t) * dr + ri] = rc;
+      rope_tab[long(t) * dr + dr / 2 + ri] = rsn;
+    }
+  }
   if (slot < 0 || slot >= num_slots) return;        // uniform over the block
   if (W % 4 == 0) {
     for (int i = 4 * threadIdx.x; i < W; i += 4 * blockDim.x)
@@ -82,12 +89,10 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / float(dc) + eps);
   for (int i = threadIdx.x; i < dc; i += blockDim.x) row[i] = row[i] * r * ldf<ActT>(gamma, i);
-  for (int i = threadIdx.x; i < dr / 2; i += blockDim.x) {
-    float c, s;
-    rope_cs(p, i, dr, theta, &c, &s);
-    float e = row[dc + 2 * i], o = row[dc + 2 * i + 1];
-    row[dc + 2 * i] = e * c - o * s;
-    row[dc + 2 * i + 1] = e * s + o * c;
+  if (ri >= 0) {
+    const float e = row[dc + 2 * ri], o = row[dc + 2 * ri + 1];
+    row[dc + 2 * ri] = e * rc - o * rsn;
+    row[dc + 2 * ri + 1] = e * rsn + o * rc;
   }
   __syncthreads();
   if (CACHE == K_F32) {
@@ -105,6 +110,18 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
     for (int i = threadIdx.x; i < W; i += blockDim.x) dst[i] = uint8_t(f_to_e4m3(__fdiv_rn(row[i], sc)));
     if (threadIdx.x == 0) cache_scale[slot] = sc;
   }
+}
+
+template <typename ActT, int CACHE>
+__global__ __launch_bounds__(256) void compress_rows_kernel(
+    int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
+    const int32_t* __restrict__ pos, const int64_t* __restrict__ slots, void* __restrict__ cache,
+    float* __restrict__ cache_scale, long num_slots, float eps, float theta, float* __restrict__ rope_tab,
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks) {
+  extern __shared__ float row[];                    // [dc + dr]
+  __shared__ float red[16];
+  compress_row<ActT, CACHE>(blockIdx.x, dc, dr, T, nsplit, acc, gamma, pos, slots, cache, cache_scale, num_slots,
+                            eps, theta, rope_tab, ctx, bt, max_blocks, row, red);
 }
 
 void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit, const float* acc,
@@ -130,13 +147,9 @@ void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit,
 
 // ------------------------------------------------------------------ RMSNorm of query latents
 template <typename ActT>
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsplit,
-                                                           const float* __restrict__ acc,
-                                                           const ActT* __restrict__ gamma,
-                                                           ActT* __restrict__ out, float eps) {
-  extern __shared__ float row[];
-  __shared__ float red[16];
-  const int t = blockIdx.x;
+__device__ __forceinline__ void rmsnorm_row(int t, int T, int n, int nsplit, const float* __restrict__ acc,
+                                            const ActT* __restrict__ gamma, ActT* __restrict__ out, float eps,
+                                            float* row, float* red) {
   float ss = 0.f;
   if (n % 4 == 0) {
     for (int i = 4 * threadIdx.x; i < n; i += 4 * blockDim.x) {
@@ -155,6 +168,53 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsp
   const float r = 1.0f / sqrtf(ss / float(n) + eps);
   for (int i = threadIdx.x; i < n; i += blockDim.x)
     stf<ActT>(out, long(t) * n + i, row[i] * r * ldf<ActT>(gamma, i));
+}
+
+template <typename ActT>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsplit,
+                                                           const float* __restrict__ acc,
+                                                           const ActT* __restrict__ gamma,
+                                                           ActT* __restrict__ out, float eps) {
+  extern __shared__ float row[];
+  __shared__ float red[16];
+  rmsnorm_row<ActT>(blockIdx.x, T, n, nsplit, acc, gamma, out, eps, row, red);
+}
+
+// Decode: the compress epilogue of the T new tokens (blocks [0, T)) and the RMSNorm of their
+// query latents (blocks [T, 2T)) in one launch; the two read disjoint partials.
+template <typename ActT, int CACHE>
+__global__ __launch_bounds__(256) void decode_rows_kernel(
+    int dc, int dr, int T, int nsplit_kv, const float* __restrict__ acc_kv, const ActT* __restrict__ gamma_kv,
+    void* __restrict__ cache, float* __restrict__ cache_scale, long num_slots, float eps, float theta,
+    float* __restrict__ rope_tab, const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks,
+    int nq, int nsplit_q, const float* __restrict__ acc_q, const ActT* __restrict__ gamma_q, ActT* __restrict__ cq) {
+  extern __shared__ float row[];                    // [max(dc + dr, nq)]
+  __shared__ float red[16];
+  const int t = blockIdx.x;
+  if (t < T)
+    compress_row<ActT, CACHE>(t, dc, dr, T, nsplit_kv, acc_kv, gamma_kv, nullptr, nullptr, cache, cache_scale,
+                              num_slots, eps, theta, rope_tab, ctx, bt, max_blocks, row, red);
+  else
+    rmsnorm_row<ActT>(t - T, T, nq, nsplit_q, acc_q, gamma_q, cq, eps, row, red);
+}
+
+bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
+                        const void* gamma_kv, void* cache_data, float* cache_scale, long num_slots, float eps,
+                        float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                        int nq, int nsplit_q, const float* acc_q, const void* gamma_q, void* cq, hipStream_t st) {
+  if (T <= 0 || act != K_BF16 || (cache != K_BF16 && cache != K_FP8) || !ctx || !rope_tab) return false;
+  const size_t sh = size_t(max(dc + dr, nq)) * sizeof(float);
+#define MLA_DR(C)                                                                                     \
+  hipLaunchKernelGGL((decode_rows_kernel<uint16_t, C>), dim3(2 * T), dim3(256), sh, st, dc, dr, T, nsplit_kv, \
+                     acc_kv, static_cast<const uint16_t*>(gamma_kv), cache_data, cache_scale, num_slots, eps, \
+                     theta, rope_tab, ctx, bt, max_blocks, nq, nsplit_q, acc_q,                        \
+                     static_cast<const uint16_t*>(gamma_q), static_cast<uint16_t*>(cq))
+  if (cache == K_BF16)
+    MLA_DR(K_BF16);
+  else
+    MLA_DR(K_FP8);
+#undef MLA_DR
+  return true;
 }
 
 void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,

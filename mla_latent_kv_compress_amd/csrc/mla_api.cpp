@@ -76,6 +76,38 @@ void enqueue_query(const Dims& d, Path path, const mla_config* cfg, const mla_we
                    nq, 0, alpha), s);
 }
 
+// Decode front on the bf16 path with a query LoRA: the kv_a and q_a projections in one launch,
+// the compress epilogue and the query-latent RMSNorm in one launch, then q_b.  Same arithmetic
+// as enqueue_compress + enqueue_query; false (nothing enqueued) if the grouped launch does not
+// apply.
+bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
+                          const void* hidden, const mla_cache* cache, int B, const DecodePlan& p, void* ws,
+                          float* rope, const int32_t* ctx, const int32_t* bt, int max_blocks, hipStream_t s) {
+  const QueryPlan& q = p.q;
+  if (path != PATH_BF16 || d.dq <= 0 || q.direct) return false;
+  float* acc_kv = reinterpret_cast<float*>(at(ws, p.comp.off_acc));
+  float* acc_q = reinterpret_cast<float*>(at(ws, q.off_qa_acc));
+  void* cq = at(ws, q.off_cq);
+  const GemmArgs g_q = gemm(path, false, K_F32, B, d.dq, d.D, q.split_a, 1, hidden, d.D, 0, w->q_a_proj, d.D, 0,
+                            acc_q, d.dq, 0);
+  const GemmArgs g_kv = gemm(path, false, K_F32, B, d.W(), d.D, p.comp.split, 1, hidden, d.D, 0, w->kv_a_proj,
+                             d.D, 0, acc_kv, d.W(), 0);
+  if (!launch_gemm_pair(g_q, g_kv, s)) return false;
+  const long num_slots = long(cache->num_blocks) * MLA_PAGE_SIZE;
+  if (!launch_decode_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
+                          w->kv_a_norm, cache->data, cache->scale, num_slots, d.eps, d.theta, rope, ctx, bt,
+                          max_blocks, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, s)) {
+    launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
+                         w->kv_a_norm, nullptr, nullptr, cache->data, cache->scale, num_slots, d.eps, d.theta, rope,
+                         ctx, bt, max_blocks, s);
+    launch_rmsnorm_rows(kdt(cfg->act_dtype), B, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, d.eps, s);
+  }
+  const long nq = long(d.H) * d.dqk();
+  launch_gemm(gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, d.dq, 0, w->q_b_proj, d.dq, 0,
+                   at(ws, q.off_q_acc), nq, 0), s);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,7 +194,11 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   int64_t* slot = reinterpret_cast<int64_t*>(at(workspace, p.off_slot));
 
   float* rope = reinterpret_cast<float*>(at(workspace, p.off_rope));
-  if (path == PATH_BF16) {
+  const bool front = enqueue_decode_front(d, path, cfg, w, hidden, cache, B, p, workspace, rope, context_lens,
+                                          block_table, max_blocks, s);
+  if (front) {
+    // compress / append and the query projection enqueued by the grouped front
+  } else if (path == PATH_BF16) {
     // the row epilogue takes each token's position and slot from its context length itself
     enqueue_compress(d, path, cfg, w, hidden, nullptr, nullptr, cache, B, p.comp, workspace, s, rope, context_lens,
                      block_table, max_blocks);
@@ -170,7 +206,7 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
     launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
     enqueue_compress(d, path, cfg, w, hidden, pos, slot, cache, B, p.comp, workspace, s, rope);
   }
-  enqueue_query(d, path, cfg, w, hidden, B, p.q, workspace, nullptr, 0.f, s);
+  if (!front) enqueue_query(d, path, cfg, w, hidden, B, p.q, workspace, nullptr, 0.f, s);
 
   // Scaled queries: sigma * log2(e) folded in, so the kernels use exp2.
   const float qscale = d.sigma * kLog2eHost;

@@ -23,6 +23,9 @@ struct GemmArgs {
   float alpha;
 };
 void launch_gemm(const GemmArgs& g, hipStream_t st);
+// Two independent fp32-output skinny GEMMs in one launch; false (nothing launched) when either
+// does not meet the skinny kernel's conditions.
+bool launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t st);
 
 // Dtype codes for cache, activations and intermediate buffers inside the kernels.
 enum { K_F32 = 0, K_BF16 = 1, K_FP8 = 2, K_F16 = 3 };
@@ -42,6 +45,12 @@ bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit
 // out[t][:] = RMSNorm(sum_s acc[s][t][:]) * gamma, in act dtype.
 void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,
                          void* out, float eps, hipStream_t st);
+// Decode, bf16 activations: the compress epilogue (positions from the context lengths, RoPE
+// table written) and the query-latent RMSNorm in one launch of 2T blocks; false if unsupported.
+bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
+                        const void* gamma_kv, void* cache_data, float* cache_scale, long num_slots, float eps,
+                        float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                        int nq, int nsplit_q, const float* acc_q, const void* gamma_q, void* cq, hipStream_t st);
 
 // Query packing from fp32 partials q_acc [nsplit][T][H*(dn+dr)]: sum, scale by `scale`,
 // RoPE on q_pe.
