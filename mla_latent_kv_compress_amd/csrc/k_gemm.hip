@@ -431,9 +431,166 @@ __global__ __launch_bounds__(256) void merge_uv_kernel(
   }
 }
 
+// The same merge + projection with the split count SPL and the latent width DC fixed at compile
+// time, so that the K loop unrolls into straight-line code with its loads kMuAhead steps ahead
+// of use (the weights of every split are likewise fetched at once): the generic kernel above
+// waits for each step's loads in turn.  Rows past B read row 0 of the partials with merge
+// weight 0 (the partials are finite), so no branch guards the loads.  The arithmetic and its
+// order are those of merge_uv_kernel.
+constexpr int kMuAhead = 4;
+template <int NT, int OUT, int SPL, int DC>
+__global__ __launch_bounds__(256) void merge_uv_fixed_kernel(
+    int B, int H, int dn, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
+  constexpr int dv = 16 * NT, half = DC / 2, nk = half / 32;
+  static_assert(nk >= kMuAhead, "prefetch depth within the K loop");
+  __shared__ f32x4_t red[2][NT][64];                // second c-half sums, [row group][tile][lane]
+  __shared__ float wts[32][SPL];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave & 1, kh = wave >> 1;
+  const int h = blockIdx.x, b0 = blockIdx.y * 32;
+  // Order of the requests: the merge statistics (every thread fetches its row's, tid & 31, so no
+  // branch splits the loads), then the first kMuAhead steps of partials and weights, and only
+  // then the wait for the statistics: the main stream is already in flight across the barrier.
+  float mj[SPL], lj[SPL];
+  {
+    const int bm = min(b0 + (tid & 31), B - 1);
+    const float* ml = part_ml + (long(bm) * SPL * H + h) * 2;
+    const long step = long(H) * 2;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      mj[j] = ml[j * step];
+      lj[j] = ml[j * step + 1];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int r = 16 * rg + (lane & 15), b = b0 + r, kq = 8 * (lane >> 4);
+  const int kbeg = kh * half;
+  const float* po = part_o + (long(b < B ? b : 0) * SPL * H + h) * DC + kbeg + kq;
+  const long pstride = long(H) * DC;                // between the splits of one (b, h)
+  const uint16_t* wuv = kv_b + (long(h) * (dn + dv) + dn + (lane & 15)) * DC + kbeg + kq;
+  bf16x8_t wf[kMuAhead][NT];
+  float4 xo[kMuAhead][SPL][2];
+#pragma unroll
+  for (int k = 0; k < kMuAhead; ++k) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) wf[k][t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * DC + 32 * k);
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      xo[k][j][0] = *reinterpret_cast<const float4*>(po + j * pstride + 32 * k);
+      xo[k][j][1] = *reinterpret_cast<const float4*>(po + j * pstride + 32 * k + 4);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    // (every thread computes its row's weights and stores them, the 8 copies of a row alike: a
+    // store guarded by tid < 32 would let the compiler sink the statistics loads behind the
+    // stream)
+    const int b = b0 + (tid & 31);
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) m = fmaxf(m, mj[j]);
+    float l = 0.f, e[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      e[j] = mj[j] == -INFINITY ? 0.f : exp2f(mj[j] - m);
+      l += e[j] * lj[j];
+    }
+    const float inv = (b < B && l > 0.f) ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) wts[tid & 31][j] = e[j] * inv;
+  }
+  __syncthreads();
+
+  float wr[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) wr[j] = wts[r][j];
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // (scheduling barriers keep the source order: the compiler would otherwise move each load
+  // next to its use and shorten the prefetch distance to nothing)
+#pragma unroll
+  for (int k = 0; k < nk; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int sl = k % kMuAhead;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const float wj = wr[j];
+      const float4 x0 = xo[sl][j][0], x1 = xo[sl][j][1];
+      v[0] += wj * x0.x; v[1] += wj * x0.y; v[2] += wj * x0.z; v[3] += wj * x0.w;
+      v[4] += wj * x1.x; v[5] += wj * x1.y; v[6] += wj * x1.z; v[7] += wj * x1.w;
+    }
+    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+    bf16x8v hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = (__bf16)v[e];                          // round to nearest even
+      lo[e] = (__bf16)(v[e] - (float)hi[e]);
+    }
+    bf16x8_t w[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t] = wf[sl][t];
+    if (k + kMuAhead < nk) {                         // refill the slot kMuAhead steps ahead
+      const int kn = 32 * (k + kMuAhead);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wf[sl][t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * DC + kn);
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        xo[sl][j][0] = *reinterpret_cast<const float4*>(po + j * pstride + kn);
+        xo[sl][j][1] = *reinterpret_cast<const float4*>(po + j * pstride + kn + 4);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, w[t], acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w[t], acc[t], 0, 0, 0);
+    }
+  }
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[rg][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  // C layout: lane holds C[4 (lane / 16) + i][lane % 16] of each 16 x 16 tile.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const f32x4_t o = acc[t] + red[rg][t][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bo = b0 + 16 * rg + 4 * (lane >> 4) + i;
+      if (bo < B) sts_<OUT>(out, (long(bo) * H + h) * dv + 16 * t + (lane & 15), o[i]);
+    }
+  }
+}
+
+template <int OUT, int SPL>
+static void launch_merge_uv_fixed(int B, int H, int dn, const float* part_o, const float* part_ml,
+                                  const void* kv_b, void* out, hipStream_t st) {
+  hipLaunchKernelGGL((merge_uv_fixed_kernel<8, OUT, SPL, 512>), dim3(H, (B + 31) / 32), dim3(256), 0, st, B, H, dn,
+                     part_o, part_ml, static_cast<const uint16_t*>(kv_b),
+                     static_cast<typename StoreT<OUT>::type*>(out));
+}
+
 bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
                             const float* part_ml, const void* kv_b, void* out, hipStream_t st) {
   if (dv != 128 || dc % 64 != 0 || splits > 256) return false;
+  if (dc == 512 && splits >= 1 && splits <= 4) {
+#define MLA_MU(SPL)                                                                                     \
+  (out_type == K_BF16 ? launch_merge_uv_fixed<S_BF16, SPL>(B, H, dn, part_o, part_ml, kv_b, out, st)    \
+                      : launch_merge_uv_fixed<S_F32, SPL>(B, H, dn, part_o, part_ml, kv_b, out, st))
+    switch (splits) {
+      case 1: MLA_MU(1); break;
+      case 2: MLA_MU(2); break;
+      case 3: MLA_MU(3); break;
+      default: MLA_MU(4); break;
+    }
+#undef MLA_MU
+    return true;
+  }
   dim3 grid(H, (B + 31) / 32);
   const size_t sh = size_t(32) * splits * sizeof(float);
   if (out_type == K_BF16)
