@@ -176,15 +176,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
 
 // ------------------------------------------------------------------ skinny bf16 GEMM (M <= 64)
 // Y = alpha X W^T for M <= 64 rows (a decode batch): the weight stream is the whole cost, so
-// each work-group owns 64 output columns and streams its [64 x K-chunk] slice of W (and the
-// matching slice of X, an L2 hit) through a ring of kSkStages LDS stages with direct
-// global->LDS loads, several stages ahead of the MFMAs.  A stage is 64 rows x 64 k of X and of W,
+// each work-group owns 64 or 96 output columns and streams its [columns x K-chunk] slice of W
+// (and the matching slice of X, an L2 hit) through a ring of LDS stages with direct
+// global->LDS loads, several stages ahead of the MFMAs.  A stage is 64 k of X (64 rows) and of W,
 // rows of 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), so the 16 rows
 // of an MFMA operand read fall on distinct banks.  Rows past M (or N) re-read the last valid
 // row; their outputs are not stored.  Requires K and the K chunk to be multiples of 64.
 namespace {
-constexpr int kSkStages = 4;
-constexpr int kSkStageBytes = 2 * 64 * 128;           // X tile + W tile
+template <int BN> constexpr int sk_stage_bytes() { return (64 + BN) * 128; }
+// Ring depth: 4 stages (16 or 20 KiB each), three stages of loads in flight.  (Measured: a
+// 7-stage ring for the one-per-CU 96-column tiles made the 236B-shaped q_b and kv_a + q_a
+// projections slower, not faster.)
+template <int BN> constexpr int sk_stages() { return 4; }
 
 __device__ __forceinline__ void sk_dma16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
@@ -216,9 +219,17 @@ struct SkinnyProb {
   float alpha;
 };
 
-// Output tile (64 rows x 64 columns from column tile nx) of batch-and-split index z.
-template <int OUT>
+// Output tile (64 rows x BN columns from column tile nx) of batch-and-split index z.  BN is 64 or
+// 96: a stage holds the X tile (64 rows x 64 k) and the W tile (BN rows x 64 k), rows of 128
+// bytes, (64 + BN) / 8 direct-load instructions of 1 KiB (8 rows each) dealt round-robin to the
+// four waves; wave (wm, wn) computes rows 32 wm .. +32 and columns BN / 2 wn .. + BN / 2.
+template <int OUT, int BN>
 __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, char* ring) {
+  constexpr int kStageB = sk_stage_bytes<BN>();
+  constexpr int S = sk_stages<BN>();
+  constexpr int NQ = (64 + BN) / 8 / 4;                  // load instructions per wave per stage
+  constexpr int NC = BN / 32;                            // 16-column tiles per wave
+  static_assert((64 + BN) % 32 == 0, "whole instructions per wave");
   const int M = p.M, N = p.N, K = p.K, kchunk = p.kchunk, nsplit = p.nsplit;
   const long lda = p.lda, ldw = p.ldw, ldc = p.ldc;
   const float alpha = p.alpha;
@@ -231,77 +242,84 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
   typename StoreT<OUT>::type* Y = static_cast<typename StoreT<OUT>::type*>(p.Y) + b * p.sy + sp * p.ssplit;
   const int k0 = sp * kchunk;
   const int nk = (min(K, k0 + kchunk) - k0) / 64;      // 64-wide K steps of this split
-  const int n0 = nx * 64;
+  const int n0 = nx * BN;
 
-  // Direct loads: wave w brings rows [16w, 16w + 16) of the X tile and of the W tile, two
-  // 1 KiB instructions each (8 rows x 128 bytes; lane i -> row + (i >> 3), stored chunk i & 7).
-  uint32_t xoff[2], woff[2];
+  // Instruction q = wave + 4 j fills KiB q of the stage: q < 8 are X rows 8q .. +7, the rest W
+  // rows 8 (q - 8) .. +7 (lane i -> row + (i >> 3), stored chunk i & 7).
+  uint32_t off[NQ];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 16 * wave + 8 * q + (lane >> 3);
+  for (int j = 0; j < NQ; ++j) {
+    const int q = wave + 4 * j;
+    const bool isx = q < 8;
+    const int r = 8 * (isx ? q : q - 8) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    xoff[q] = uint32_t((long(min(r, M - 1)) * lda + 8 * c) * 2);
-    woff[q] = uint32_t((long(min(n0 + r, N - 1)) * ldw + 8 * c) * 2);
+    off[j] = isx ? uint32_t((long(min(r, M - 1)) * lda + 8 * c) * 2) : uint32_t((long(min(n0 + r, N - 1)) * ldw + 8 * c) * 2);
   }
-  auto issue = [&](int j) {
-    if (j >= nk) return;
-    char* st = ring + (j % kSkStages) * kSkStageBytes;
-    const long kb = long(k0 + 64 * j) * 2;
+  auto issue = [&](int jj) {
+    if (jj >= nk) return;
+    char* st = ring + (jj % S) * kStageB;
+    const long kb = long(k0 + 64 * jj) * 2;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      sk_dma16(reinterpret_cast<const char*>(X) + kb, xoff[q], sk_lds_addr(st + (16 * wave + 8 * q) * 128));
-      sk_dma16(reinterpret_cast<const char*>(W) + kb, woff[q], sk_lds_addr(st + 8192 + (16 * wave + 8 * q) * 128));
+    for (int j = 0; j < NQ; ++j) {
+      const int q = wave + 4 * j;                       // uniform: q < 8 selects X
+      sk_dma16(reinterpret_cast<const char*>(q < 8 ? X : W) + kb, off[j], sk_lds_addr(st + q * 1024));
     }
   };
-  auto wait_for = [&](int j) {                          // stage j landed (this wave's part)
-    const int ahead = min(nk - 1, j + kSkStages - 2) - j;
-    if (ahead >= 2) sk_wait_vm<8>();
-    else if (ahead == 1) sk_wait_vm<4>();
-    else sk_wait_vm<0>();
+  auto wait_for = [&](int jj) {                         // stage jj landed (this wave's part)
+    const int ahead = min(nk - 1, jj + S - 2) - jj;     // later stages already issued
+    static_assert(S <= 7 && 5 * NQ < 64, "wait counts");
+    switch (ahead) {
+      case 5: sk_wait_vm<(S >= 7 ? 5 : 0) * NQ>(); break;
+      case 4: sk_wait_vm<(S >= 6 ? 4 : 0) * NQ>(); break;
+      case 3: sk_wait_vm<(S >= 5 ? 3 : 0) * NQ>(); break;
+      case 2: sk_wait_vm<2 * NQ>(); break;
+      case 1: sk_wait_vm<NQ>(); break;
+      default: sk_wait_vm<0>(); break;
+    }
   };
 
-  f32x4_t acc[2][2];
+  f32x4_t acc[2][NC];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NC; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // operand rows and their chunk XOR
-  int arow[2], brow[2];
+  int arow[2], brow[NC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    arow[i] = 32 * wm + 16 * i + (lane & 15);
-    brow[i] = 32 * wn + 16 * i + (lane & 15);
-  }
+  for (int i = 0; i < 2; ++i) arow[i] = 32 * wm + 16 * i + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) brow[i] = (BN / 2) * wn + 16 * i + (lane & 15);
   const int g = lane >> 4;
 
 #pragma unroll
-  for (int j = 0; j < kSkStages - 1; ++j) issue(j);
+  for (int j = 0; j < S - 1; ++j) issue(j);
   for (int i = 0; i < nk; ++i) {
     wait_for(i);
     sk_barrier();                                       // stage i visible; stage i - 1 consumed
-    issue(i + kSkStages - 1);
-    const char* st = ring + (i % kSkStages) * kSkStageBytes;
+    issue(i + S - 1);
+    const char* st = ring + (i % S) * kStageB;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t af[2], bf[2];
+      bf16x8_t af[2], bf[NC];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
         af[t] = *reinterpret_cast<const bf16x8_t*>(st + arow[t] * 128 + 16 * ((4 * kk + g) ^ ((arow[t] >> 1) & 7)));
+#pragma unroll
+      for (int t = 0; t < NC; ++t)
         bf[t] = *reinterpret_cast<const bf16x8_t*>(st + 8192 + brow[t] * 128 +
                                                    16 * ((4 * kk + g) ^ ((brow[t] >> 1) & 7)));
-      }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
     }
   }
   // C layout: lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile.
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int gn = n0 + 32 * wn + 16 * c + (lane & 15);
+    for (int c = 0; c < NC; ++c) {
+      const int gn = n0 + (BN / 2) * wn + 16 * c + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int gm = 32 * wm + 16 * a + 4 * (lane >> 4) + r;
@@ -310,24 +328,24 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     }
 }
 
-template <int OUT>
+template <int OUT, int BN>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyProb p) {
-  __shared__ __attribute__((aligned(1024))) char ring[kSkStages * kSkStageBytes];
-  skinny_tile<OUT>(p, blockIdx.x, blockIdx.z, ring);
+  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN>()];
+  skinny_tile<OUT, BN>(p, blockIdx.x, blockIdx.z, ring);
 }
 
 // Two independent skinny problems in one launch: work-groups [0, tiles0) take p0's tiles,
 // the rest p1's (one launch instead of two dependent-free ones back to back).
-template <int OUT>
+template <int OUT, int BN>
 __global__ __launch_bounds__(256) void gemm_skinny_pair_kernel(SkinnyProb p0, SkinnyProb p1, int tiles0) {
-  __shared__ __attribute__((aligned(1024))) char ring[kSkStages * kSkStageBytes];
+  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN>()];
   const int id = blockIdx.x;
   if (id < tiles0) {
-    const int nx = (p0.N + 63) / 64;
-    skinny_tile<OUT>(p0, id % nx, id / nx, ring);
+    const int nx = (p0.N + BN - 1) / BN;
+    skinny_tile<OUT, BN>(p0, id % nx, id / nx, ring);
   } else {
-    const int nx = (p1.N + 63) / 64;
-    skinny_tile<OUT>(p1, (id - tiles0) % nx, (id - tiles0) / nx, ring);
+    const int nx = (p1.N + BN - 1) / BN;
+    skinny_tile<OUT, BN>(p1, (id - tiles0) % nx, (id - tiles0) / nx, ring);
   }
 }
 
@@ -732,8 +750,16 @@ template <bool NN, int OUT>
 static void launch_bf16_shape(const GemmArgs& g, hipStream_t st) {
   long tiles_big = long((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch * g.nsplit;
   if (skinny_ok(g)) {
-    dim3 grid((g.N + 63) / 64, 1, g.batch * g.nsplit);
-    hipLaunchKernelGGL(gemm_skinny_kernel<OUT>, grid, dim3(256), 0, st, skinny_prob(g));
+    // 96-column tiles when they fill the CUs in whole rounds and 64-column tiles do not (fewer,
+    // better balanced work-groups, each re-reading X for more columns)
+    const long z = long(g.batch) * g.nsplit;
+    if (g.N % 96 == 0 && (g.N / 96) * z % 256 == 0 && ((g.N + 63) / 64) * z % 256 != 0) {
+      hipLaunchKernelGGL((gemm_skinny_kernel<OUT, 96>), dim3(g.N / 96, 1, unsigned(z)), dim3(256), 0, st,
+                         skinny_prob(g));
+      return;
+    }
+    hipLaunchKernelGGL((gemm_skinny_kernel<OUT, 64>), dim3((g.N + 63) / 64, 1, unsigned(z)), dim3(256), 0, st,
+                       skinny_prob(g));
     return;
   }
   if (g.M <= 64)
@@ -754,11 +780,17 @@ static void launch_bf16_out(const GemmArgs& g, hipStream_t st) {
 bool launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0 || b.M <= 0 || b.N <= 0 || b.batch <= 0) return false;
   if (!skinny_ok(a) || !skinny_ok(b) || a.out != K_F32 || b.out != K_F32) return false;
-  const long t0 = long((a.N + 63) / 64) * a.batch * a.nsplit;
-  const long t1 = long((b.N + 63) / 64) * b.batch * b.nsplit;
+  // 96-column tiles when both widths allow them (the split planned for the pair assumes so)
+  const int bn = (a.N % 96 == 0 && b.N % 96 == 0) ? 96 : 64;
+  const long t0 = long((a.N + bn - 1) / bn) * a.batch * a.nsplit;
+  const long t1 = long((b.N + bn - 1) / bn) * b.batch * b.nsplit;
   if (t0 + t1 > (1L << 31) - 1) return false;
-  hipLaunchKernelGGL(gemm_skinny_pair_kernel<S_F32>, dim3(unsigned(t0 + t1)), dim3(256), 0, st, skinny_prob(a),
-                     skinny_prob(b), int(t0));
+  if (bn == 96)
+    hipLaunchKernelGGL((gemm_skinny_pair_kernel<S_F32, 96>), dim3(unsigned(t0 + t1)), dim3(256), 0, st,
+                       skinny_prob(a), skinny_prob(b), int(t0));
+  else
+    hipLaunchKernelGGL((gemm_skinny_pair_kernel<S_F32, 64>), dim3(unsigned(t0 + t1)), dim3(256), 0, st,
+                       skinny_prob(a), skinny_prob(b), int(t0));
   return true;
 }
 

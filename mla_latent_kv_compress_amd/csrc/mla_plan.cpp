@@ -75,17 +75,27 @@ SplitK gemm_splitk(long M, long N, long K, int tile_m, int tile_n) {
   return s;
 }
 
-int plan_compress(const Dims& d, Path path, long T, Layout& L, CompressPlan* p) {
+SplitK pair_splitk(long M, long N0, long N1, long K) {
+  if (M > 64 || N0 % 96 != 0 || N1 % 96 != 0 || K % 64 != 0 || K <= 0) return SplitK{0, 0};
+  const long tiles = N0 / 96 + N1 / 96;
+  long n = 256 / tiles;
+  if (n < 1) n = 1;
+  const long chunk = rup(cdiv(K, n), 64);
+  return SplitK{int(cdiv(K, chunk)), int(chunk)};
+}
+
+int plan_compress(const Dims& d, Path path, long T, Layout& L, CompressPlan* p, const SplitK* force) {
   (void)path;
-  p->split = gemm_splitk(T, d.W(), d.D, 64, 64);
+  p->split = force ? *force : gemm_splitk(T, d.W(), d.D, 64, 64);
   p->off_acc = L.take(size_t(p->split.n) * T * d.W() * 4);
   return MLA_OK;
 }
 
-static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q, bool allow_direct) {
+static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q, bool allow_direct,
+                       const SplitK* force_a = nullptr) {
   long nq = long(d.H) * d.dqk();
   if (d.dq > 0) {
-    q->split_a = gemm_splitk(T, d.dq, d.D, 64, 64);
+    q->split_a = force_a ? *force_a : gemm_splitk(T, d.dq, d.D, 64, 64);
     q->off_qa_acc = L.take(size_t(q->split_a.n) * T * d.dq * 4);
     q->off_cq = L.take(size_t(T) * d.dq * (path == PATH_F32 ? 4 : 2));
     q->split_b = gemm_splitk(T, nq, d.dq, 64, 64);
@@ -121,8 +131,13 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   Layout L;
   p->splits = splits > 0 ? splits : auto_splits(d, path, B, max_blocks);
   size_t act = path == PATH_F32 ? 4 : 2;
-  plan_compress(d, path, B, L, &p->comp);
-  plan_query(d, path, B, L, &p->q, false);
+  // The decode front launches the kv_a and q_a projections together (bf16 path with a query
+  // LoRA): one K split for both, with the pair's tile shape.
+  SplitK pair{0, 0};
+  if (path == PATH_BF16 && d.dq > 0) pair = pair_splitk(B, d.dq, d.W(), d.D);
+  const SplitK* force = pair.n > 0 ? &pair : nullptr;
+  plan_compress(d, path, B, L, &p->comp, force);
+  plan_query(d, path, B, L, &p->q, false, force);
   p->off_pos = L.take(size_t(B) * 4);
   p->off_slot = L.take(size_t(B) * 8);
   p->off_qnope = L.take(size_t(B) * d.H * d.dn * act);

@@ -43,12 +43,16 @@ struct SplitK {
   int chunk;
 };
 SplitK gemm_splitk(long M, long N, long K, int tile_m, int tile_n);
+// One K split shared by two skinny GEMMs (M <= 64 rows, N0 and N1 columns, K deep) launched
+// together with 96-column tiles, sized so that the pair fills 256 CUs in one round; n = 0 when
+// that launch does not apply (N0 or N1 not a multiple of 96, M > 64, K not a multiple of 64).
+SplitK pair_splitk(long M, long N0, long N1, long K);
 
 struct CompressPlan {
   SplitK split;
   size_t off_acc;        // fp32 [split.n][T][W]
 };
-int plan_compress(const Dims& d, Path path, long T, Layout& L, CompressPlan* p);
+int plan_compress(const Dims& d, Path path, long T, Layout& L, CompressPlan* p, const SplitK* force = nullptr);
 
 struct QueryPlan {            // q path for T tokens, shared by decode and prefill
   SplitK split_a, split_b;
