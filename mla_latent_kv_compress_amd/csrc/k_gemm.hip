@@ -217,7 +217,14 @@ struct SkinnyProb {
   void* Y;
   long ldc, sy, ssplit;
   float alpha;
+  float* Y2;                 // (query-split output only) fp32 q_pe
 };
+
+// Output mode of the decode query projection (q_b, N = H x 192): columns 0..127 of each head
+// (q_nope) are stored as bf16(alpha q) to Y [M][H][128], the A operand the absorb kernel feeds
+// straight to the matrix core, and columns 128..191 (q_pe) as fp32 q to Y2 [M][H][64], which
+// the absorb kernel rotates.  This is the rounding that kernel applies to the fp32 projection.
+constexpr int kOutQSplit = 7;
 
 // Output tile (64 rows x BN columns from column tile nx) of batch-and-split index z.  BN is 64 or
 // 96: a stage holds the X tile (64 rows x 64 k) and the W tile (BN rows x 64 k), rows of 128
@@ -323,7 +330,17 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int gm = 32 * wm + 16 * a + 4 * (lane >> 4) + r;
-        if (gm < M && gn < N) sts_<OUT>(Y, long(gm) * ldc + gn, alpha * acc[a][c][r]);
+        if (gm < M && gn < N) {
+          if constexpr (OUT == kOutQSplit) {
+            const int hh = gn / 192, cc = gn - 192 * hh, HH = N / 192;
+            if (cc < 128)
+              reinterpret_cast<uint16_t*>(p.Y)[(long(gm) * HH + hh) * 128 + cc] = f2bf(alpha * acc[a][c][r]);
+            else
+              p.Y2[(long(gm) * HH + hh) * 64 + cc - 128] = acc[a][c][r];
+          } else {
+            sts_<OUT>(Y, long(gm) * ldc + gn, alpha * acc[a][c][r]);
+          }
+        }
       }
     }
 }
@@ -627,9 +644,12 @@ bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, 
 // reads it with the transposing ds_read_b64_tr_b16 as the B operand (8 consecutive d per lane);
 // the A operand (64 decode rows x 32 d) comes straight from the fp32 projection.  The extra
 // column block blockIdx.x = dc / 64 applies RoPE to q_pe with the token angles in rope_tab.
-template <int DN>
+// QS: the query comes split by the projection's epilogue (q_nope as bf16(scale q) [B][H][DN],
+// q_pe as fp32 [B][H][dr]) instead of as fp32 partials; the products and roundings are the same.
+template <int DN, bool QS>
 __global__ __launch_bounds__(256) void absorb_rope_kernel(
     int B, int H, int dr, int dc, int dv, int nsplit, const float* __restrict__ q_acc,
+    const uint16_t* __restrict__ q_nope16, const float* __restrict__ q_pe32,
     const float* __restrict__ rope_tab, float scale, const uint16_t* __restrict__ kv_b,
     uint16_t* __restrict__ qhat) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[DN * 64];
@@ -649,7 +669,8 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
       const int b = b0 + e / half, pi = e % half;
       if (b >= B) continue;
       const float c = rope_tab[long(b) * dr + pi], sn = rope_tab[long(b) * dr + half + pi];
-      const float ev = qsum(b, DN + 2 * pi), ov = qsum(b, DN + 2 * pi + 1);
+      const float* qp = q_pe32 + (long(b) * H + h) * dr + 2 * pi;
+      const float ev = QS ? qp[0] : qsum(b, DN + 2 * pi), ov = QS ? qp[1] : qsum(b, DN + 2 * pi + 1);
       uint16_t* o = qhat + (long(b) * H + h) * (dc + dr) + dc + 2 * pi;
       o[0] = f2bf(scale * (ev * c - ov * sn));
       o[1] = f2bf(scale * (ev * sn + ov * c));
@@ -674,6 +695,11 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
 #pragma unroll
   for (int ks = 0; ks < DN / 32; ++ks) {
     typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+    bf16x8v a;
+    if constexpr (QS) {
+      a = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const bf16x8_t*>(
+                                          q_nope16 + (long(min(b, B - 1)) * H + h) * DN + 32 * ks + 8 * g));
+    } else {
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (b < B) {
       const float* src = qh + long(b) * nq + 32 * ks + 8 * g;
@@ -684,9 +710,9 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
         v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
       }
     }
-    bf16x8v a;
 #pragma unroll
     for (int j = 0; j < 8; ++j) a[j] = (__bf16)(scale * v[j]);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       typedef short s16x4v __attribute__((ext_vector_type(4)));
@@ -709,11 +735,18 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
 }
 
 bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit, const float* q_acc,
-                        const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st) {
+                        const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st,
+                        const void* q_nope16, const float* q_pe32) {
   if (dn != 128 || dc % 64 != 0 || dr % 2 != 0 || B <= 0) return false;
   dim3 grid(dc / 64 + 1, H, (B + 63) / 64);
-  hipLaunchKernelGGL(absorb_rope_kernel<128>, grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, q_acc, rope_tab,
-                     scale, static_cast<const uint16_t*>(kv_b), static_cast<uint16_t*>(qhat));
+  if (q_nope16 && q_pe32)
+    hipLaunchKernelGGL((absorb_rope_kernel<128, true>), grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, nullptr,
+                       static_cast<const uint16_t*>(q_nope16), q_pe32, rope_tab, scale,
+                       static_cast<const uint16_t*>(kv_b), static_cast<uint16_t*>(qhat));
+  else
+    hipLaunchKernelGGL((absorb_rope_kernel<128, false>), grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, q_acc,
+                       nullptr, nullptr, rope_tab, scale, static_cast<const uint16_t*>(kv_b),
+                       static_cast<uint16_t*>(qhat));
   return true;
 }
 
@@ -743,6 +776,7 @@ static SkinnyProb skinny_prob(const GemmArgs& g) {
   p.W = static_cast<const uint16_t*>(g.W); p.ldw = g.ldw; p.sw = g.sw;
   p.Y = g.Y; p.ldc = g.ldc; p.sy = g.sy; p.ssplit = g.ssplit;
   p.alpha = g.alpha;
+  p.Y2 = nullptr;
   return p;
 }
 
@@ -775,6 +809,17 @@ static void launch_bf16_out(const GemmArgs& g, hipStream_t st) {
   if (g.out == K_BF16) launch_bf16_shape<NN, S_BF16>(g, st);
   else if (g.out == K_F16) launch_bf16_shape<NN, S_F16>(g, st);
   else launch_bf16_shape<NN, S_F32>(g, st);
+}
+
+bool launch_q_split_gemm(const GemmArgs& g, float* q_pe, hipStream_t st) {
+  if (!skinny_ok(g) || g.nsplit != 1 || g.batch != 1 || g.N % 192 != 0) return false;
+  SkinnyProb p = skinny_prob(g);
+  p.Y2 = q_pe;
+  if (g.N % 96 == 0 && (g.N / 96) % 256 == 0)
+    hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 96>), dim3(g.N / 96, 1, 1), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 64>), dim3(g.N / 64, 1, 1), dim3(256), 0, st, p);
+  return true;
 }
 
 bool launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t st) {

@@ -82,7 +82,9 @@ void enqueue_query(const Dims& d, Path path, const mla_config* cfg, const mla_we
 // apply.
 bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
                           const void* hidden, const mla_cache* cache, int B, const DecodePlan& p, void* ws,
-                          float* rope, const int32_t* ctx, const int32_t* bt, int max_blocks, hipStream_t s) {
+                          float* rope, const int32_t* ctx, const int32_t* bt, int max_blocks, float qscale,
+                          bool* qsplit, hipStream_t s) {
+  *qsplit = false;
   const QueryPlan& q = p.q;
   if (path != PATH_BF16 || d.dq <= 0 || q.direct) return false;
   float* acc_kv = reinterpret_cast<float*>(at(ws, p.comp.off_acc));
@@ -103,6 +105,18 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
     launch_rmsnorm_rows(kdt(cfg->act_dtype), B, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, d.eps, s);
   }
   const long nq = long(d.H) * d.dqk();
+  // q_b with the split epilogue (q_nope as bf16(scale q), q_pe fp32, in the q_acc region) when
+  // it applies; the absorb kernel then reads half the bytes.
+  if (q.split_b.n == 1 && d.dn == 128 && d.dr == 64) {
+    char* qn = at(ws, q.off_q_acc);
+    float* qpe = reinterpret_cast<float*>(qn + size_t(B) * d.H * d.dn * 2);
+    if (launch_q_split_gemm(gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, d.dq, 0, w->q_b_proj, d.dq,
+                                 0, qn, nq, 0, qscale),
+                            qpe, s)) {
+      *qsplit = true;
+      return true;
+    }
+  }
   launch_gemm(gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, d.dq, 0, w->q_b_proj, d.dq, 0,
                    at(ws, q.off_q_acc), nq, 0), s);
   return true;
@@ -194,8 +208,11 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   int64_t* slot = reinterpret_cast<int64_t*>(at(workspace, p.off_slot));
 
   float* rope = reinterpret_cast<float*>(at(workspace, p.off_rope));
+  // Scaled queries: sigma * log2(e) folded in, so the kernels use exp2.
+  const float qscale = d.sigma * kLog2eHost;
+  bool qsplit = false;
   const bool front = enqueue_decode_front(d, path, cfg, w, hidden, cache, B, p, workspace, rope, context_lens,
-                                          block_table, max_blocks, s);
+                                          block_table, max_blocks, qscale, &qsplit, s);
   if (front) {
     // compress / append and the query projection enqueued by the grouped front
   } else if (path == PATH_BF16) {
@@ -208,15 +225,17 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   }
   if (!front) enqueue_query(d, path, cfg, w, hidden, B, p.q, workspace, nullptr, 0.f, s);
 
-  // Scaled queries: sigma * log2(e) folded in, so the kernels use exp2.
-  const float qscale = d.sigma * kLog2eHost;
   void* qnope = at(workspace, p.off_qnope);
   void* qhat = at(workspace, p.off_qhat);
   const float* qacc = reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc));
   // Absorb: qhat[b][h][0:dc] = q_nope[b][h] . W_UK^h  (W_UK^h = kv_b_proj rows of head h's k_nope),
   // qhat[b][h][dc:] = RoPE(q_pe[b][h]); one kernel on the bf16 path.
+  const void* qn16 = qsplit ? at(workspace, p.q.off_q_acc) : nullptr;
+  const float* qpe32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc) + size_t(B) * d.H * d.dn * 2)
+                              : nullptr;
   if (!(path == PATH_BF16 && launch_absorb_rope(B, d.H, d.dn, d.dr, d.dc, d.dv, p.q.split_b.n, qacc, rope, qscale,
-                                                w->kv_b_proj, qhat, s))) {
+                                                w->kv_b_proj, qhat, s, qn16, qpe32))) {
+    if (qsplit) return MLA_ERR_UNSUPPORTED;       // (cannot happen: both need dn 128, dr 64, dc 512)
     if (path == PATH_BF16) launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
     launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n, qacc, pos, qscale, d.theta, qnope, qhat,
                   nullptr, s);

@@ -40,7 +40,12 @@ void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit,
 // qhat[b][h] = [ W_UK^h^T bf16(scale q_nope) | bf16(scale RoPE(q_pe)) ] (bf16), with the
 // angles of each token from rope_tab ([B][dr]: cos | sin).  False if the shape does not apply.
 bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit, const float* q_acc,
-                        const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st);
+                        const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st,
+                        const void* q_nope16 = nullptr, const float* q_pe32 = nullptr);
+// Decode q_b projection (no K split, N = H x 192) whose epilogue stores q_nope as bf16(alpha q)
+// to g.Y [M][H][128] and q_pe as fp32 to q_pe [M][H][64] (the absorb kernel's QS input); false
+// (nothing launched) if the skinny kernel does not apply.
+bool launch_q_split_gemm(const GemmArgs& g, float* q_pe, hipStream_t st);
 
 // out[t][:] = RMSNorm(sum_s acc[s][t][:]) * gamma, in act dtype.
 void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,
