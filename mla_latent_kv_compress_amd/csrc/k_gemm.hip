@@ -473,23 +473,24 @@ __global__ __launch_bounds__(256) void merge_uv_kernel(
 // weight 0 (the partials are finite), so no branch guards the loads.  The arithmetic and its
 // order are those of merge_uv_kernel.
 constexpr int kMuAhead = 4;
-template <int NT, int OUT, int SPL, int DC>
-__global__ __launch_bounds__(256) void merge_uv_fixed_kernel(
+// NKH: the latent range is cut into NKH parts, one per wave of a row group (2 x NKH waves).
+template <int NT, int OUT, int SPL, int DC, int NKH>
+__global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
     int B, int H, int dn, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
-  constexpr int dv = 16 * NT, half = DC / 2, nk = half / 32;
+  constexpr int dv = 16 * NT, half = DC / NKH, nk = half / 32;
   static_assert(nk >= kMuAhead, "prefetch depth within the K loop");
-  __shared__ f32x4_t red[2][NT][64];                // second c-half sums, [row group][tile][lane]
+  __shared__ f32x4_t red[2][NKH - 1][NT][64];       // other parts' sums, [row group][part][tile][lane]
   __shared__ float wts[32][SPL];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = wave & 1, kh = wave >> 1;
+  const int rg = wave & 1, kh = wave >> 1;          // row group, latent part
   const int h = blockIdx.x, b0 = blockIdx.y * 32;
   // Order of the requests: the merge statistics (every thread fetches its row's, tid & 31, so no
   // branch splits the loads), then the first kMuAhead steps of partials and weights, and only
   // then the wait for the statistics: the main stream is already in flight across the barrier.
   float mj[SPL], lj[SPL];
   {
-    const int bm = min(b0 + (tid & 31), B - 1);
+    const int bm = min(b0 + (tid & 31), B - 1);       // (tid & 31: every thread, rows alike)
     const float* ml = part_ml + (long(bm) * SPL * H + h) * 2;
     const long step = long(H) * 2;
 #pragma unroll
@@ -584,16 +585,19 @@ __global__ __launch_bounds__(256) void merge_uv_fixed_kernel(
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w[t], acc[t], 0, 0, 0);
     }
   }
-  if (kh == 1) {
+  if (kh > 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[rg][t][lane] = acc[t];
+    for (int t = 0; t < NT; ++t) red[rg][kh - 1][t][lane] = acc[t];
   }
   __syncthreads();
-  if (kh == 1) return;
-  // C layout: lane holds C[4 (lane / 16) + i][lane % 16] of each 16 x 16 tile.
+  if (kh > 0) return;
+  // C layout: lane holds C[4 (lane / 16) + i][lane % 16] of each 16 x 16 tile.  The parts are
+  // added in order.
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const f32x4_t o = acc[t] + red[rg][t][lane];
+    f32x4_t o = acc[t];
+#pragma unroll
+    for (int q = 0; q < NKH - 1; ++q) o += red[rg][q][t][lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int bo = b0 + 16 * rg + 4 * (lane >> 4) + i;
@@ -605,7 +609,9 @@ __global__ __launch_bounds__(256) void merge_uv_fixed_kernel(
 template <int OUT, int SPL>
 static void launch_merge_uv_fixed(int B, int H, int dn, const float* part_o, const float* part_ml,
                                   const void* kv_b, void* out, hipStream_t st) {
-  hipLaunchKernelGGL((merge_uv_fixed_kernel<8, OUT, SPL, 512>), dim3(H, (B + 31) / 32), dim3(256), 0, st, B, H, dn,
+  constexpr int kParts = 4;
+  hipLaunchKernelGGL((merge_uv_fixed_kernel<8, OUT, SPL, 512, kParts>), dim3(H, (B + 31) / 32), dim3(128 * kParts),
+                     0, st, B, H, dn,
                      part_o, part_ml, static_cast<const uint16_t*>(kv_b),
                      static_cast<typename StoreT<OUT>::type*>(out));
 }
