@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   // Work-group -> (sequence, split, head group).  Work-groups are dealt to the 8 XCDs
   // round-robin; with xcd_map the head groups of one (sequence, split) land on the same XCD in
   // consecutive rounds.
-  const int G = H / kHeads;
+  const int G = (H + kHeads - 1) / kHeads;                  // the last group may be partial
   int b, sp, hg;
   {
     const int unit = blockIdx.x;
@@ -256,13 +256,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
 
   // ---- score-wave state
   // Query fragments (B operand of the score product): Qhat[head 32 hh + 16 nt + li][32 ks + 8 g .. +7].
+  // Heads past H (a partial last group, e.g. 16 heads in a group of 64) get a zero query: their
+  // scores are 0, their sums finite, and nothing of theirs is stored.
   bf16x8_t qf[2][kKS];
   if (scorer) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const uint16_t* q = qhat + (long(b) * H + hbase + 32 * hh + 16 * nt + li) * kDW + 8 * g;
+      const int head = hbase + 32 * hh + 16 * nt + li;
+      const uint16_t* q = qhat + (long(b) * H + min(head, H - 1)) * kDW + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) qf[nt][ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
+      for (int ks = 0; ks < kKS; ++ks)
+        qf[nt][ks] = head < H ? *reinterpret_cast<const bf16x8_t*>(q + 32 * ks) : bf16x8_t{};
     }
   }
   float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
@@ -456,6 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     if (mt_w == 0 && g == 0) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
+        if (hbase + hrow(nt) >= H) continue;
         const long row = (long(b) * splits + sp) * H + hbase + hrow(nt);
         part_ml[row * 2] = m_ref[nt];
         part_ml[row * 2 + 1] = lsum[nt];
@@ -502,6 +507,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     const long row0 = (long(b) * splits + sp) * H + hbase;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
+      if (hbase + 32 * nt + ph >= H) continue;
       float* dst = part_o + (row0 + 32 * nt + ph) * kDC + 128 * wave + 4 * (lane >> 5);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
@@ -514,8 +520,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
 }
 
 bool launch_decode_attn_v2(const DecodeAttnArgs& a, hipStream_t st) {
-  if (a.H % kHeads != 0 || a.dc != kDC || a.dr != kDR) return false;
-  const long units = long(a.B) * a.splits * (a.H / kHeads);
+  if (a.H % 16 != 0 || a.dc != kDC || a.dr != kDR) return false;
+  const long units = long(a.B) * a.splits * ((a.H + kHeads - 1) / kHeads);
   const int xcd_map = (a.B % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(decode_attn_latent_kernel, dim3(unsigned(units)), dim3(kThreads), 0, st, a.H, a.splits,
                      a.max_blocks, xcd_map, static_cast<const uint16_t*>(a.qhat), static_cast<const uint16_t*>(a.cache),
