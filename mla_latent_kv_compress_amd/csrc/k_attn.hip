@@ -281,7 +281,7 @@ void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t
                        static_cast<const float*>(a.cache), a.block_table, a.ctx, a.part_o, a.part_ml);
     return;
   }
-  if (cache == K_BF16 && a.heads_per_group == 64 && launch_decode_attn_v2(a, st)) return;
+  if (a.heads_per_group == 64 && launch_decode_attn_v2(cache, a, st)) return;
   // heads_per_group = NW * 16: 64 -> 4 waves, 32 -> 2 waves, 16 -> 1 wave.
   const int G = a.H / a.heads_per_group;
   const long units = (long(a.B) * a.splits + 7) / 8 * 8;

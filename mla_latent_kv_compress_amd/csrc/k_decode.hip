@@ -37,6 +37,15 @@
 // and it costs two extra passes only on such splits).  The partial state (m, l, O) is consistent
 // for the log-sum-exp merge whatever m is.  Rows of a stage beyond the context re-read the last
 // valid row (finite data) and get p = 0.
+//
+// fp8 cache (e4m3 codes plus one fp32 scale per token): the same kernel with 576-byte rows, so a
+// 32-token stage is 18 KiB of codes plus the stage's 32 scales, and the ring holds 8 stages.  The
+// codes are converted exactly to bf16 at the operand reads (v_cvt_scalef32_pk_bf16_fp8 with scale
+// 1) and the token scale s_t is applied outside the products: score = s_t (code . Qhat), and the
+// value product takes p s_t as its weight (l still sums p).  The score operand is one 128-bit read
+// per lane covering two K steps (K permuted the same way in Qhat); the value operand is one
+// ds_read_b64_tr_b8 (lane i of each 16-lane group: column c0 + i over the 8 rows addressed by
+// lanes 2j, 2j + 1).  Stored chunk of row r, logical chunk c: c ^ ((r >> 2) & 3).
 #include <type_traits>
 
 #include "mla_device.h"
@@ -47,13 +56,29 @@ namespace mla {
 namespace {
 
 constexpr int kDC = 512, kDR = 64, kDW = kDC + kDR;
-constexpr int kRowBytes = kDW * 2;                    // 1152
-constexpr int kPageBytes = kPage * kRowBytes;         // 73728
 constexpr int kStage = 32;                            // tokens per pipeline stage
-constexpr int kStageBytes = kStage * kRowBytes;       // 36864
-constexpr int kRing = 4;
 constexpr int kThreads = 512;                         // 4 score waves + 4 value waves
-constexpr int kLoads = kStageBytes / 16 / 256;        // 9 direct loads per value-wave thread per stage
+
+// Per cache type: row bytes, stage codes, ring slot size and depth, direct loads per value-wave
+// thread per stage.
+template <bool FP8> struct Geo;
+template <> struct Geo<false> {
+  static constexpr int kRowBytes = kDW * 2;           // 1152
+  static constexpr int kCodeBytes = kStage * kRowBytes;   // 36864
+  static constexpr int kSlot = kCodeBytes;
+  static constexpr int kRing = 4;
+  static constexpr int kLoads = kCodeBytes / 16 / 256;    // 9 dwordx4 loads
+};
+template <> struct Geo<true> {
+  static constexpr int kRowBytes = kDW;               // 576
+  static constexpr int kCodeBytes = kStage * kRowBytes;   // 18432: 18 dwordx4 loads per stage
+  static constexpr int kScaleOff = kCodeBytes;        // two copies of the stage's scales (256 B each)
+  static constexpr int kSlot = kCodeBytes + 512;
+  static constexpr int kRing = 8;
+  // Waves 0, 1: code loads 4k + w, k < 5; waves 2, 3: code loads 4k + w, k < 4, and one dword
+  // load of the stage's scales.
+  static constexpr int kLoads = 5;
+};
 constexpr int kKS = kDW / 32;                         // 18 score K steps
 constexpr int kHeads = 64;                            // heads per work-group
 constexpr int kPBytes = kHeads * kStage * 2;          // 4096
@@ -130,25 +155,62 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Offset, within a stage, of the 16 bytes that lane `lane` of direct-load instruction k of wave
 // `wave` fetches: instruction k of wave w fills LDS bytes [(4k + w) KiB, +1 KiB) of the stage;
-// lane i supplies stored chunk (4k + w) * 64 + i, i.e. row r = chunk / 72, logical chunk
-// (chunk % 72) ^ rsw(r).  Rows at or beyond `valid` re-read row valid - 1.
+// lane i supplies stored chunk (4k + w) * 64 + i.  bf16 rows (72 chunks): row r = chunk / 72,
+// logical chunk (chunk % 72) ^ rsw(r).  fp8 rows (36 chunks): row r = chunk / 36, logical chunk
+// (chunk % 36) ^ ((r >> 2) & 3).  Rows at or beyond `valid` re-read row valid - 1.
+template <bool FP8>
 __device__ __forceinline__ uint32_t stage_offset(int k, int wave, int lane, int valid) {
+  constexpr int kChunks = Geo<FP8>::kRowBytes / 16;
   const int idx = (4 * k + wave) * 64 + lane;
-  const int r = idx / 72, cp = idx - r * 72;
-  const int c = cp ^ rsw(r);
+  const int r = idx / kChunks, cp = idx - r * kChunks;
+  const int c = FP8 ? (cp ^ ((r >> 2) & 3)) : (cp ^ rsw(r));
   const int rs = r < valid ? r : valid - 1;
-  return uint32_t(rs * kRowBytes + c * 16);
+  return uint32_t(rs * Geo<FP8>::kRowBytes + c * 16);
+}
+
+// Direct load of 4 bytes per lane: lane i's word at base + off lands at LDS byte lds + 4 i.
+__device__ __forceinline__ void dma4(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// Wait until at most A * L of this wave's direct loads are outstanding, A the largest of
+// A_MAX, ..., 1 not above `ahead` (0 if none).
+template <int A, int L>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (A == 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= A) wait_vm<A * L>();
+    else wait_ahead<A - 1, L>(ahead);
+  }
+}
+
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+// Eight e4m3 codes (two words, code j in byte j) to eight bf16 values, exactly.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w0), 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w0), 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w1), 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w1), 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 }  // namespace
 
+template <bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     int H, int splits, int max_blocks, int xcd_map, const uint16_t* __restrict__ qhat,
-    const uint16_t* __restrict__ cache, const int32_t* __restrict__ bt, const int32_t* __restrict__ ctx_lens,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(1024))) char smem[kRing * kStageBytes + 2 * kPBytes];
+    const void* __restrict__ cache, const float* __restrict__ cache_scale, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ ctx_lens, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  using Gm = Geo<FP8>;
+  constexpr int kRowBytes = Gm::kRowBytes, kSlot = Gm::kSlot, kRing = Gm::kRing, kLoads = Gm::kLoads;
+  constexpr int kPageBytes = kPage * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kRing * kSlot + 2 * kPBytes];
   char* const ring = smem;
-  char* const pbase = smem + kRing * kStageBytes;          // P of stage j in pbase + (j & 1) * kPBytes
+  char* const pbase = smem + kRing * kSlot;                // P of stage j in pbase + (j & 1) * kPBytes
+  auto slot = [&](int j) { return ring + (j & (kRing - 1)) * kSlot; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -189,62 +251,93 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   uint32_t full_off[kLoads];             // offsets of a stage whose rows are all cached
   if (!scorer) {
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) full_off[k] = stage_offset(k, wave, lane, kStage);
+    for (int k = 0; k < kLoads; ++k) full_off[k] = stage_offset<FP8>(k, wave, lane, kStage);
   }
-  auto issue = [&](int j) {              // loads of stage j (of this split) into ring slot j % 4
+  // Loads of stage j (of this split) into ring slot j % kRing.  fp8: the last load of waves 2
+  // and 3 fetches the stage's scales (lane i: token i % 32) into their own copy.
+  auto issue = [&](int j) {
     if (j >= n) return;
-    char* dst = ring + (j & 3) * kStageBytes;
-    const char* src = cbase + long(btab[(s0 + j) >> 1]) * kPageBytes + ((s0 + j) & 1) * kStageBytes;
+    char* dst = slot(j);
+    const long page = btab[(s0 + j) >> 1];
+    const int half = (s0 + j) & 1;
+    const char* src = cbase + page * kPageBytes + half * Gm::kCodeBytes;
     const int valid = stage_valid(j);
+    constexpr int kCode = FP8 ? kLoads - 1 : kLoads;      // code loads every wave issues
     if (valid == kStage) {
 #pragma unroll
-      for (int k = 0; k < kLoads; ++k) dma16(src, full_off[k], lds_addr(dst + (4 * k + wave) * 1024));
+      for (int k = 0; k < kCode; ++k) dma16(src, full_off[k], lds_addr(dst + (4 * k + wave) * 1024));
     } else {
       int ln = lane;
       asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int k = 0; k < kLoads; ++k)
-        dma16(src, stage_offset(k, wave, ln, valid), lds_addr(dst + (4 * k + wave) * 1024));
+      for (int k = 0; k < kCode; ++k)
+        dma16(src, stage_offset<FP8>(k, wave, ln, valid), lds_addr(dst + (4 * k + wave) * 1024));
+    }
+    if constexpr (FP8) {
+      if (wave < 2) {
+        dma16(src, valid == kStage ? full_off[kLoads - 1] : stage_offset<FP8>(kLoads - 1, wave, lane, valid),
+              lds_addr(dst + (4 * (kLoads - 1) + wave) * 1024));
+      } else {
+        const char* ssrc = reinterpret_cast<const char*>(cache_scale) + (page * kPage + kStage * half) * 4;
+        const int t = min(lane & (kStage - 1), valid - 1);
+        dma4(ssrc, uint32_t(4 * t), lds_addr(dst + Gm::kScaleOff + 256 * (wave - 2)));
+      }
     }
   };
   // Wait until stage j is in LDS, stages up to `last` having been issued (in order).
-  auto wait_stage = [&](int j, int last) {
-    const int ahead = min(n - 1, last) - j;
-    if (ahead >= 2) wait_vm<2 * kLoads>();
-    else if (ahead == 1) wait_vm<kLoads>();
-    else wait_vm<0>();
-  };
+  auto wait_stage = [&](int j, int last) { wait_ahead<kRing - 2, kLoads>(min(n - 1, last) - j); };
 
   // ---- shared LDS addressing
-  // Score operand offsets: row 16 mt + li, logical chunk 4 ks + g, stored at
-  // (4 ks + g) ^ rsw(li) = 4 (ks ^ y) + x.
-  // A score wave owns token tile mt_w (tokens [16 mt_w, 16 mt_w + 16) of every stage) and head
-  // half hh (heads [32 hh, 32 hh + 32) of the group); rsw(16 mt_w + li) = rsw(li).
+  // Score operand offsets.  A score wave owns token tile mt_w (tokens [16 mt_w, 16 mt_w + 16) of
+  // every stage) and head half hh (heads [32 hh, 32 hh + 32) of the group).
+  // bf16: row 16 mt + li, logical chunk 4 ks + g, stored at (4 ks + g) ^ rsw(li) = 4 (ks ^ y) + x
+  // (rsw(16 mt_w + li) = rsw(li)).
+  // fp8: one 16-byte read per lane for K steps 2m, 2m + 1: row 16 mt + li, logical chunk 4m + g,
+  // stored at 4m + (g ^ ((li >> 2) & 3)); bytes 0-7 feed step 2m, bytes 8-15 step 2m + 1, so K
+  // value 8 g + j of step 2m + e is latent column 64m + 16g + 8e + j (Qhat is loaded to match).
   const int mt_w = wave & 1, hh = wave >> 1;
   const int sx = g ^ (rsw(li) & 3), sy = rsw(li) >> 2;
-  const int s_row = (16 * mt_w + li) * kRowBytes + 16 * sx;
+  const int s_row = (16 * mt_w + li) * kRowBytes + 16 * (FP8 ? (g ^ ((li >> 2) & 3)) : sx);
   const int s_even = s_row + 64 * sy;                      // ks even: + 64 ks
   const int s_odd = s_row - 64 * sy;                       // ks odd:  + 64 ks
   auto score_a = [&](const char* st, int ks) {
     return *reinterpret_cast<const bf16x8_t*>(st + ((ks & 1) ? s_odd : s_even) + 64 * ks);
   };
-  // Transposing reads for the value product: lane reads row 8 (lane >> 5) + 4 rd + (li >> 2)
-  // (+16 per K step), element column 128 w + 32 ct + 16 ((lane >> 4) & 1) + 4 (li & 3).
+  auto score_raw = [&](const char* st, int m) { return *reinterpret_cast<const uint4*>(st + s_row + 64 * m); };
+  // Transposing reads for the value product.
+  // bf16: lane reads row 8 (lane >> 5) + 4 rd + (li >> 2) (+16 per K step), element column
+  // 128 w + 32 ct + 16 ((lane >> 4) & 1) + 4 (li & 3).
+  // fp8: lane reads row 8 (lane >> 5) + (li >> 1) (+16 per K step), byte column
+  // 128 w + 32 ct + 16 ((lane >> 4) & 1) + 8 (li & 1); the row's chunk XOR (r >> 2) & 3 is
+  // (2 (lane >> 5) + (li >> 3)), so column tiles ct = 2u + e sit at t_even / t_odd + 64 u.
   int t_even[2], t_odd[2];
+  if constexpr (FP8) {
+    const int f1 = lane >> 5, f0 = li >> 3, e = (lane >> 4) & 1;
+    const int rr = 8 * f1 + (li >> 1);
+    const int base = rr * kRowBytes + 16 * (8 * wave + (e ^ f0)) + 8 * (li & 1);
+    t_even[0] = base + 32 * f1;
+    t_odd[0] = base + 32 * (1 - f1);
+    t_even[1] = t_odd[1] = 0;
+  } else {
 #pragma unroll
-  for (int rd = 0; rd < 2; ++rd) {
-    const int rr = 8 * (lane >> 5) + 4 * rd + (li >> 2);
-    const int gs = rsw(rr);
-    const int x = 2 * ((lane >> 4) & 1) + ((li & 3) >> 1);
-    const int base = rr * kRowBytes + 256 * wave + 16 * (x ^ (gs & 3)) + 8 * (li & 1);
-    t_even[rd] = base + 64 * (gs >> 2);
-    t_odd[rd] = base - 64 * (gs >> 2);
+    for (int rd = 0; rd < 2; ++rd) {
+      const int rr = 8 * (lane >> 5) + 4 * rd + (li >> 2);
+      const int gs = rsw(rr);
+      const int x = 2 * ((lane >> 4) & 1) + ((li & 3) >> 1);
+      const int base = rr * kRowBytes + 256 * wave + 16 * (x ^ (gs & 3)) + 8 * (li & 1);
+      t_even[rd] = base + 64 * (gs >> 2);
+      t_odd[rd] = base - 64 * (gs >> 2);
+    }
   }
   auto val_a = [&](const char* st, int ks, int ct) {
     const int add = 64 * ct + ks * 16 * kRowBytes;
     const char* p0 = st + ((ct & 1) ? t_odd[0] : t_even[0]) + add;
     const char* p1 = st + ((ct & 1) ? t_odd[1] : t_even[1]) + add;
     return join(tr_read(p0), tr_read(p1));
+  };
+  auto val_raw = [&](const char* st, int ks, int ct) {
+    const char* p = st + ((ct & 1) ? t_odd[0] : t_even[0]) + 64 * (ct >> 1) + ks * 16 * kRowBytes;
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i_t __attribute__((address_space(3)))*)(p));
   };
   const int ph = lane & 31;
   // P operand: Pbuf[head 32 nt + ph][tokens 16 ks + 8 (lane >> 5) .. +7].
@@ -255,7 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   };
 
   // ---- score-wave state
-  // Query fragments (B operand of the score product): Qhat[head 32 hh + 16 nt + li][32 ks + 8 g .. +7].
+  // Query fragments (B operand of the score product): Qhat[head 32 hh + 16 nt + li][32 ks + 8 g .. +7]
+  // (fp8: the permuted K order above).
   // Heads past H (a partial last group, e.g. 16 heads in a group of 64) get a zero query: their
   // scores are 0, their sums finite, and nothing of theirs is stored.
   bf16x8_t qf[2][kKS];
@@ -263,10 +357,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int head = hbase + 32 * hh + 16 * nt + li;
-      const uint16_t* q = qhat + (long(b) * H + min(head, H - 1)) * kDW + 8 * g;
+      const uint16_t* q = qhat + (long(b) * H + min(head, H - 1)) * kDW;
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks)
-        qf[nt][ks] = head < H ? *reinterpret_cast<const bf16x8_t*>(q + 32 * ks) : bf16x8_t{};
+      for (int ks = 0; ks < kKS; ++ks) {
+        const int col = FP8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
+        qf[nt][ks] = head < H ? *reinterpret_cast<const bf16x8_t*>(q + col) : bf16x8_t{};
+      }
     }
   }
   float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
@@ -277,15 +373,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   float* const xm = reinterpret_cast<float*>(pbase + kPBytes);
   float* const lx = reinterpret_cast<float*>(pbase + kPBytes + 2 * kHeads * 4);
   auto hrow = [&](int nt) { return 32 * hh + 16 * nt + li; };
+  // fp8: scales of the lane's four tokens 16 mt_w + 4 g + j of the current stage (read by scores).
+  f32x4_t tsc = f32x4_t{1.f, 1.f, 1.f, 1.f};
 
   // Scores of the stage's tile (C layout: lane holds tokens 16 mt_w + 4 g + j, j < 4, of head
-  // hrow(nt)), masked beyond the `valid` cached tokens, and each head's max over the tile.
+  // hrow(nt)), scaled by the token scales (fp8), masked beyond the `valid` cached tokens, and
+  // each head's max over the tile.
   auto mask = [&](int valid, f32x4_t (&v)[2]) {
     const int lim = valid - 16 * mt_w - 4 * g;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[nt][j] = j < lim ? s[nt][0][j] + s[nt][1][j] : -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        float x = s[nt][0][j] + s[nt][1][j];
+        if constexpr (FP8) x *= tsc[j];
+        v[nt][j] = j < lim ? x : -INFINITY;
+      }
   };
   auto tile = [&](int valid, f32x4_t (&v)[2], float (&mx)[2]) {
     mask(valid, v);
@@ -303,7 +406,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     return r;
   };
   // p = 2^(s - m) against the reference (an empty split keeps m = -inf and uses 0: its masked
-  // scores still give p = 0), packed to bf16 for the value product; l accumulates the fp32 p.
+  // scores still give p = 0), packed to bf16 for the value product (fp8: p s_t); l accumulates
+  // the fp32 p.
   auto weigh = [&](const f32x4_t (&v)[2], uint2 (&pk)[2]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -314,8 +418,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
         p[j] = __builtin_amdgcn_exp2f(v[nt][j] - m_use);   // 0 for masked tokens
         psum += p[j];
       }
-      pk[nt] = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
       l_run[nt] += psum;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] *= tsc[j];
+      }
+      pk[nt] = make_uint2(pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3]));
     }
   };
   auto store_p = [&](char* pb, const uint2 (&pk)[2]) {
@@ -328,12 +436,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   };
   // Score tile of one stage: each K-tile fragment feeds both head tiles; K steps alternate
   // between two accumulators per head tile (four independent MFMA chains); fragments are read
-  // kScoreRing - 1 K steps ahead of use.
+  // kScoreRing - 1 K steps ahead of use (fp8: 16-byte reads two K-step pairs ahead).
   auto scores = [&](const char* st) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int q = 0; q < 2; ++q) s[nt][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FP8) {
+      tsc = *reinterpret_cast<const f32x4_t*>(st + Gm::kScaleOff + 4 * (16 * mt_w + 4 * g));
+      constexpr int kR = 3, kM = kKS / 2;
+      uint4 raw[kR];
+#pragma unroll
+      for (int j = 0; j < kR - 1; ++j) raw[j] = score_raw(st, j);
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        const int mn = m + kR - 1;
+        if (mn < kM) raw[mn % kR] = score_raw(st, mn);
+        const uint4 r = raw[m % kR];
+        const bf16x8_t a0 = fp8x8_to_bf16(r.x, r.y), a1 = fp8x8_to_bf16(r.z, r.w);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[nt][2 * m], s[nt][0], 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[nt][2 * m + 1], s[nt][1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     bf16x8_t a[kScoreRing];
 #pragma unroll
     for (int j = 0; j < kScoreRing - 1; ++j) a[j] = score_a(st, j);
@@ -354,6 +484,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) pf[ks][nt] = p_frag(pb, ks, nt);
+    if constexpr (FP8) {                                 // codes read two steps ahead of use
+      v2i_t raw[3];
+      raw[0] = val_raw(st, 0, 0);
+      raw[1] = val_raw(st, 0, 1);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u + 2 < 8) raw[(u + 2) % 3] = val_raw(st, (u + 2) >> 2, (u + 2) & 3);
+        const int ks = u >> 2, ct = u & 3;
+        const bf16x8_t av = fp8x8_to_bf16(uint32_t(raw[u % 3][0]), uint32_t(raw[u % 3][1]));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks][nt], o[ct][nt], 0, 0, 0);
+      }
+      return;
+    }
     bf16x8_t av[2];
     av[0] = val_a(st, 0, 0);
 #pragma unroll
@@ -370,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   // work-group barriers.  Pass structure: an accumulating pass against the first stage's max;
   // if any score outgrew its reference by kSlack, a scores-only pass for the exact maxima and an
   // accumulating pass against them.  Stage j's P lives in P buffer j % 2; stage j in ring slot
-  // j % 4.
+  // j % kRing.
   int* flags = reinterpret_cast<int*>(pbase);
   // Every wave calls this at the end of a pass; score waves also add their partner's row sums.
   auto restart_needed = [&](bool over, float (&lsum)[2]) {
@@ -424,7 +569,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
         if (i + 1 < n) {
           f32x4_t v[2];
           uint2 pk[2];
-          scores(ring + ((i + 1) & 3) * kStageBytes);
+          scores(slot(i + 1));
           mask(stage_valid(i + 1), v);
           if (kMode == kChecked) over |= beyond(v);
           weigh(v, pk);
@@ -447,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       for (int i = 0; i < n; ++i) {
         f32x4_t v[2];
         float mx[2];
-        scores(ring + (i & 3) * kStageBytes);
+        scores(slot(i));
         tile(stage_valid(i), v, mx);
         m_ref[0] = fmaxf(m_ref[0], mx[0]);
         m_ref[1] = fmaxf(m_ref[1], mx[1]);
@@ -474,32 +619,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[ct][nt][e] = 0.f;
-      issue(0);
-      issue(1);
-      issue(2);
-      wait_stage(0, 2);
+      for (int j = 0; j < kRing - 1; ++j) issue(j);
+      wait_stage(0, kRing - 2);
       lds_barrier();                            // stage 0 loaded
       lds_barrier();                            // (score waves exchange maxima)
-      wait_stage(1, 2);
+      wait_stage(1, kRing - 2);
       lds_barrier();
       for (int i = 0; i < n; ++i) {
-        issue(i + 3);                           // into the slot of stage i - 1, free since the last barrier
-        values(ring + (i & 3) * kStageBytes, pbase + (i & 1) * kPBytes);
-        wait_stage(i + 2, i + 3);
+        issue(i + kRing - 1);                   // into the slot of stage i - 1, free since the last barrier
+        values(slot(i), pbase + (i & 1) * kPBytes);
+        wait_stage(i + 2, i + kRing - 1);
         lds_barrier();
       }
       return false;
     };
     float unused[2] = {0.f, 0.f};
     if (restart_needed(accumulate(), unused)) {
-      issue(0);
-      issue(1);
-      issue(2);
-      wait_stage(0, 2);
+      for (int j = 0; j < kRing - 1; ++j) issue(j);
+      wait_stage(0, kRing - 2);
       lds_barrier();
       for (int i = 0; i < n; ++i) {
-        issue(i + 3);
-        wait_stage(i + 1, i + 3);
+        issue(i + kRing - 1);
+        wait_stage(i + 1, i + kRing - 1);
         lds_barrier();
       }
       restart_needed(accumulate(), unused);
@@ -519,13 +660,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   }
 }
 
-bool launch_decode_attn_v2(const DecodeAttnArgs& a, hipStream_t st) {
+bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t st) {
   if (a.H % 16 != 0 || a.dc != kDC || a.dr != kDR) return false;
+  if (cache_type != K_BF16 && cache_type != K_FP8) return false;
   const long units = long(a.B) * a.splits * ((a.H + kHeads - 1) / kHeads);
   const int xcd_map = (a.B % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(decode_attn_latent_kernel, dim3(unsigned(units)), dim3(kThreads), 0, st, a.H, a.splits,
-                     a.max_blocks, xcd_map, static_cast<const uint16_t*>(a.qhat), static_cast<const uint16_t*>(a.cache),
-                     a.block_table, a.ctx, a.part_o, a.part_ml);
+  const auto kern = cache_type == K_FP8 ? decode_attn_latent_kernel<true> : decode_attn_latent_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(unsigned(units)), dim3(kThreads), 0, st, a.H, a.splits, a.max_blocks, xcd_map,
+                     static_cast<const uint16_t*>(a.qhat), a.cache, a.cache_scale, a.block_table, a.ctx,
+                     a.part_o, a.part_ml);
   return true;
 }
 

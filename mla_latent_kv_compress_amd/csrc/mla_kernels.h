@@ -85,8 +85,8 @@ struct DecodeAttnArgs {
   float* part_o; float* part_ml;
 };
 void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st);
-// 64-head work-groups over a bf16 cache (k_decode.hip); false if the shape does not apply.
-bool launch_decode_attn_v2(const DecodeAttnArgs& a, hipStream_t st);
+// 64-head work-groups over a bf16 or fp8 cache (k_decode.hip); false if the shape does not apply.
+bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t st);
 
 // Log-sum-exp merge of split partials, normalised.  fp32 path: otilde [B][H][dc] fp32; bf16
 // path: otilde [B][H][2*dc] = [hi | lo] with hi = bf16(v), lo = bf16(v - hi).

@@ -86,6 +86,7 @@ CASES = {
     "dsv2_fp8": (DSV2, "bf16", "fp8", [0, 70, 300]),
     "lite_bf16": (LITE, "bf16", "bf16", [1, 127, 450]),
     "lite_fp8": (LITE, "bf16", "fp8", [5, 200]),
+    "dsv2_fp8_long": (DSV2, "bf16", "fp8", [31, 1000, 2047]),
 }
 
 
