@@ -50,6 +50,7 @@
 
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "mla_plan.h"
 
 namespace mla {
 
@@ -203,7 +204,8 @@ template <bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     int H, int splits, int max_blocks, int xcd_map, const uint16_t* __restrict__ qhat,
     const void* __restrict__ cache, const float* __restrict__ cache_scale, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ ctx_lens, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ order, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
   using Gm = Geo<FP8>;
   constexpr int kRowBytes = Gm::kRowBytes, kSlot = Gm::kSlot, kRing = Gm::kRing, kLoads = Gm::kLoads;
   constexpr int kPageBytes = kPage * kRowBytes;
@@ -217,9 +219,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   const bool scorer = wid < 4;                             // else a value wave
   const int wave = wid & 3;                                // index within the role
   const int g = lane >> 4, li = lane & 15;
-  // Work-group -> (sequence, split, head group).  Work-groups are dealt to the 8 XCDs
+  // Work-group -> (sequence slot, split, head group).  Work-groups are dealt to the 8 XCDs
   // round-robin; with xcd_map the head groups of one (sequence, split) land on the same XCD in
-  // consecutive rounds.
+  // consecutive rounds.  Slots go to sequences in `order` (longest first) when it is given, so
+  // the long sequences' work-groups are dispatched first and the short ones fill in behind them.
   const int G = (H + kHeads - 1) / kHeads;                  // the last group may be partial
   int b, sp, hg;
   {
@@ -236,6 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       b = k2 / splits;
       sp = k2 - b * splits;
     }
+    if (order) b = order[b];
   }
   const int hbase = hg * kHeads;
   const int ctx = ctx_lens[b];
@@ -660,14 +664,36 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   }
 }
 
+// Sequences ranked by context length, longest first, ties by index: order[rank] = sequence.
+__global__ __launch_bounds__(1024) void seq_order_kernel(int B, const int32_t* __restrict__ ctx,
+                                                         int32_t* __restrict__ order) {
+  __shared__ int32_t len[kOrderMax];
+  for (int i = threadIdx.x; i < B; i += 1024) len[i] = ctx[i];
+  __syncthreads();
+  for (int t = threadIdx.x; t < B; t += 1024) {
+    const int c = len[t];
+    int r = 0;
+    for (int u = 0; u < B; ++u) {
+      const int cu = len[u];
+      r += (cu > c || (cu == c && u < t)) ? 1 : 0;
+    }
+    order[r] = t;
+  }
+}
+
 bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t st) {
   if (a.H % 16 != 0 || a.dc != kDC || a.dr != kDR) return false;
   if (cache_type != K_BF16 && cache_type != K_FP8) return false;
   const long units = long(a.B) * a.splits * ((a.H + kHeads - 1) / kHeads);
   const int xcd_map = (a.B % 8 == 0) ? 1 : 0;
+  const int32_t* order = nullptr;
+  if (a.order && a.B <= kOrderMax) {
+    hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, st, a.B, a.ctx, a.order);
+    order = a.order;
+  }
   const auto kern = cache_type == K_FP8 ? decode_attn_latent_kernel<true> : decode_attn_latent_kernel<false>;
   hipLaunchKernelGGL(kern, dim3(unsigned(units)), dim3(kThreads), 0, st, a.H, a.splits, a.max_blocks, xcd_map,
-                     static_cast<const uint16_t*>(a.qhat), a.cache, a.cache_scale, a.block_table, a.ctx,
+                     static_cast<const uint16_t*>(a.qhat), a.cache, a.cache_scale, a.block_table, a.ctx, order,
                      a.part_o, a.part_ml);
   return true;
 }

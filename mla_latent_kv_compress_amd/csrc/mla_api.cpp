@@ -251,6 +251,7 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   a.block_table = block_table; a.max_blocks = max_blocks; a.ctx = context_lens;
   a.part_o = reinterpret_cast<float*>(at(workspace, p.off_part_o));
   a.part_ml = reinterpret_cast<float*>(at(workspace, p.off_part_ml));
+  a.order = p.ordered ? reinterpret_cast<int32_t*>(at(workspace, p.off_order)) : nullptr;
   if (ev_attn_begin) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_begin), s);
   launch_decode_attn(act, kdt(cfg->cache_dtype), a, s);
   if (ev_attn_end) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_end), s);

@@ -83,9 +83,12 @@ struct DecodeAttnArgs {
   const int32_t* block_table; int max_blocks;
   const int32_t* ctx;
   float* part_o; float* part_ml;
+  int32_t* order = nullptr;   // [B] scratch: sequences by length, longest first (64-head kernel)
 };
 void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st);
 // 64-head work-groups over a bf16 or fp8 cache (k_decode.hip); false if the shape does not apply.
+// With a.order set, a first kernel ranks the sequences by context length (a.B <= kOrderMax) and
+// the work-groups take them longest first.
 bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t st);
 
 // Log-sum-exp merge of split partials, normalised.  fp32 path: otilde [B][H][dc] fp32; bf16

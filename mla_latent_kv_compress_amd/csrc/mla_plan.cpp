@@ -9,6 +9,10 @@ namespace {
 inline long cdiv(long a, long b) { return (a + b - 1) / b; }
 inline long rup(long a, long b) { return cdiv(a, b) * b; }
 constexpr long kMaxDim = 1 << 20;
+constexpr long kDecodeRound = 256;      // decode work-groups resident at once (one per CU)
+constexpr long kRaggedRounds = 2;
+constexpr long kRaggedTokens = 4096;    // block tables at least this long may hold ragged lengths
+constexpr long kPageTokens = 64;
 }  // namespace
 
 size_t dtype_size(int dt) {
@@ -118,9 +122,14 @@ int decode_heads_per_group(const Dims& d, Path path) {
 }
 
 int auto_splits(const Dims& d, Path path, int B, int max_blocks) {
-  long groups = cdiv(d.H, decode_heads_per_group(d, path));
+  const int hpg = decode_heads_per_group(d, path);
+  long groups = cdiv(d.H, hpg);
   long wgs = long(B) * groups;
-  long target = path == PATH_BF16 ? 256 : 512;
+  long target = path == PATH_BF16 ? kDecodeRound : 512;
+  // A batch that already fills a round of the 64-head kernel with long contexts: the lengths may
+  // be ragged, so cut every sequence in kRaggedRounds pieces (taken longest first) and let the
+  // short pieces fill in behind the long ones.
+  if (hpg == 64 && wgs >= kDecodeRound && long(max_blocks) * kPageTokens >= kRaggedTokens) target = kRaggedRounds * kDecodeRound;
   long s = cdiv(target, wgs);
   long most = max_blocks / 2 > 1 ? max_blocks / 2 : 1;
   if (s > most) s = most;
@@ -147,6 +156,9 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   p->off_qhat = L.take(size_t(B) * d.H * d.W() * act);
   p->off_part_o = L.take(size_t(B) * p->splits * d.H * d.dc * 4);
   p->off_part_ml = L.take(size_t(B) * p->splits * d.H * 2 * 4);
+  const int hpg = decode_heads_per_group(d, path);
+  p->ordered = hpg == 64 && B <= kOrderMax && long(B) * p->splits * cdiv(d.H, hpg) > kDecodeRound;
+  p->off_order = L.take(size_t(B) * 4);
   p->off_otilde = L.take(size_t(B) * d.H * d.dc * (path == PATH_F32 ? 4 : 2 * 2));
   p->bytes = L.top;
   return MLA_OK;

@@ -68,8 +68,14 @@ struct QueryPlan {            // q path for T tokens, shared by decode and prefi
 // else the largest of 64/32/16 dividing H; 1 on the fp32 path.
 int decode_heads_per_group(const Dims& d, Path path);
 
+// Longest batch for which the 64-head decode kernel takes the sequences longest first.
+constexpr int kOrderMax = 2048;
+
 struct DecodePlan {
   int splits;
+  bool ordered;               // rank the sequences by length before the attention (more than one
+                              // round of work-groups on the 64-head kernel)
+  size_t off_order;           // int32 [B]
   CompressPlan comp;
   QueryPlan q;
   size_t off_pos;             // int32 [B]

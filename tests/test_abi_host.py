@@ -144,3 +144,17 @@ def test_workspace_sizes_and_splits():
         assert 1 <= s <= 64
     c = cfg()
     assert L.mla_decode_num_splits(ctypes.byref(c), 64, 129) * 64 * 2 >= 256   # fills 256 CUs
+
+
+def test_decode_split_choice_for_the_workloads():
+    """Splits the library picks: enough 64-head work-groups (two head groups at 128 heads) for one
+    round over 256 CUs; a batch that fills a round by itself with block tables of 4096+ tokens gets
+    two rounds, since its lengths may be ragged and the work-groups go longest first."""
+    L = api.lib()
+    bf16, fp8 = cfg(DSV2, "bf16", "bf16"), cfg(DSV2, "bf16", "fp8")
+    assert L.mla_decode_num_splits(ctypes.byref(bf16), 64, 129) == 2            # 64 x 8193 tokens
+    assert L.mla_decode_num_splits(ctypes.byref(bf16), 4, 2049) == 32           # 4 x 131072 tokens
+    assert L.mla_decode_num_splits(ctypes.byref(fp8), 128, 512) == 2            # ragged 512..32768
+    assert L.mla_decode_num_splits(ctypes.byref(fp8), 128, 32) == 1             # short contexts: one round
+    lite = cfg(LITE, "bf16", "bf16")
+    assert L.mla_decode_num_splits(ctypes.byref(lite), 32, 65) == 8             # 16 heads: one group

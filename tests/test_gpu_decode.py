@@ -175,6 +175,21 @@ def test_decode_loud_token_restart(cache):
         assert e <= TOL["fp8" if cache == "fp8" else "bf16"], e
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_ragged_batch_taken_longest_first(cache):
+    """Ragged lengths over more work-groups than one round: the sequences are ranked by length on
+    the GPU and dispatched longest first; every sequence must still get its own result."""
+    lengths = [33, 2000, 64, 1200, 0, 640, 3100, 257]
+    log(f"decode ragged, ranked ({cache} cache)")
+    layer = Layer(DSV2, "bf16", cache, seed=5)
+    batch = DecodeBatch(layer, wl(DSV2, "bf16", cache, len(lengths)), seed=5, lengths=lengths)
+    out = batch.run(num_splits=20).float().cpu().numpy()       # 8 x 20 x 2 head groups = 320 work-groups
+    for b in range(len(lengths)):
+        e = rel_err(out[b], decode_reference(layer, batch, b, seed=5))
+        log(f"  seq {b} ctx {lengths[b] + 1}: rel err {e:.2e}")
+        assert e <= TOL[cache if cache == "fp8" else "bf16"], (b, e)
+
+
 def test_bf16_output():
     log("decode bf16 output")
     layer = Layer(DSV2, "bf16", "bf16", seed=1, out_dtype="bf16")
