@@ -617,8 +617,17 @@ static void launch_merge_uv_fixed(int B, int H, int dn, const float* part_o, con
 }
 
 bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
-                            const float* part_ml, const void* kv_b, void* out, hipStream_t st) {
+                            const float* part_ml, const void* kv_b, void* out, hipStream_t st, float* otilde,
+                            float* ml1) {
   if (dv != 128 || dc % 64 != 0 || splits > 256) return false;
+  if (dc == 512 && splits > 4 && otilde && ml1) {
+    // Many splits: merge them first (every partial read once, one work-group per (b, h)), then
+    // project the single merged state.
+    launch_merge_splits(B, H, dc, splits, part_o, part_ml, otilde, ml1, st);
+    splits = 1;
+    part_o = otilde;
+    part_ml = ml1;
+  }
   if (dc == 512 && splits >= 1 && splits <= 4) {
 #define MLA_MU(SPL)                                                                                     \
   (out_type == K_BF16 ? launch_merge_uv_fixed<S_BF16, SPL>(B, H, dn, part_o, part_ml, kv_b, out, st)    \

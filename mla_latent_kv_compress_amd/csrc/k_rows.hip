@@ -404,6 +404,63 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int sp
   }
 }
 
+// The same merge for many splits ahead of the fused merge + W_UV kernel, fp32 out: otilde[b][h]
+// (dc % 4 == 0) and ml1[b][h] = (0, 1), the state of one already-normalised split.  A work-group
+// of 128 threads per (b, h) reads four columns per thread and eight splits per step, so the
+// partials of every split are in flight together.
+__global__ __launch_bounds__(128) void merge_splits_kernel(int H, int dc, int splits, const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           float* __restrict__ otilde, float* __restrict__ ml1) {
+  extern __shared__ float wts[];                    // [splits] normalised split weights
+  __shared__ float red[16];
+  const int h = blockIdx.x, b = blockIdx.y;
+  float m = -INFINITY;
+  for (int s = threadIdx.x; s < splits; s += blockDim.x) m = fmaxf(m, part_ml[((long(b) * splits + s) * H + h) * 2]);
+  m = block_max(m, red);
+  float l = 0.f;
+  for (int s = threadIdx.x; s < splits; s += blockDim.x) {
+    const float* ml = part_ml + ((long(b) * splits + s) * H + h) * 2;
+    const float w = ml[0] == -INFINITY ? 0.f : exp2f(ml[0] - m);
+    wts[s] = w;
+    l += w * ml[1];
+  }
+  l = block_sum(l, red);                            // also orders the wts writes before the reads
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const long stride = long(H) * dc;                 // between consecutive splits of one (b, h)
+  const float* po = part_o + (long(b) * splits * H + h) * dc;
+  for (int c = 4 * threadIdx.x; c < dc; c += 4 * blockDim.x) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+      float4 x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const float4*>(po + (s + j) * stride + c);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = wts[s + j];
+        v.x += w * x[j].x; v.y += w * x[j].y; v.z += w * x[j].z; v.w += w * x[j].w;
+      }
+    }
+    for (; s < splits; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(po + s * stride + c);
+      const float w = wts[s];
+      v.x += w * x.x; v.y += w * x.y; v.z += w * x.z; v.w += w * x.w;
+    }
+    *reinterpret_cast<float4*>(otilde + (long(b) * H + h) * dc + c) =
+        make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+  }
+  if (threadIdx.x == 0) {
+    ml1[(long(b) * H + h) * 2] = 0.f;
+    ml1[(long(b) * H + h) * 2 + 1] = 1.f;
+  }
+}
+
+void launch_merge_splits(int B, int H, int dc, int splits, const float* part_o, const float* part_ml, float* otilde,
+                         float* ml1, hipStream_t st) {
+  hipLaunchKernelGGL(merge_splits_kernel, dim3(H, B), dim3(128), size_t(splits) * 4, st, H, dc, splits, part_o,
+                     part_ml, otilde, ml1);
+}
+
 void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
                          const float* part_ml, void* otilde, hipStream_t st) {
   if (act == K_F32)

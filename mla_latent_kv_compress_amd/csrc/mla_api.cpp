@@ -260,7 +260,9 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   // out[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  The bf16 path
   // merges the split partials inside the projection kernel.
   if (path == PATH_BF16 && launch_decode_merge_uv(kdt(cfg->out_dtype), B, d.H, d.dc, d.dn, d.dv, p.splits,
-                                                  a.part_o, a.part_ml, w->kv_b_proj, out, s))
+                                                  a.part_o, a.part_ml, w->kv_b_proj, out, s,
+                                                  reinterpret_cast<float*>(otilde),
+                                                  reinterpret_cast<float*>(at(workspace, p.off_ml1))))
     return finish();
   launch_decode_merge(act, B, d.H, d.dc, p.splits, a.part_o, a.part_ml, otilde, s);
   // On the bf16 path otilde is [hi | lo] (2 dc wide) and both halves meet the same weight row.

@@ -95,8 +95,13 @@ bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t 
 // path: otilde [B][H][2*dc] = [hi | lo] with hi = bf16(v), lo = bf16(v - hi).
 // Merge of the split partials fused with the W_UV projection (bf16 path, dv = 128):
 // out[b][h] = W_UV^h Otilde[b][h], out fp32 or bf16 per out_type; false if the shape does not apply.
+// With more than 4 splits (dc 512) and the two fp32 scratch buffers otilde [B][H][dc] and
+// ml1 [B][H][2], the splits are merged by a first kernel and the projection reads the result.
 bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
-                            const float* part_ml, const void* kv_b, void* out, hipStream_t st);
+                            const float* part_ml, const void* kv_b, void* out, hipStream_t st,
+                            float* otilde = nullptr, float* ml1 = nullptr);
+void launch_merge_splits(int B, int H, int dc, int splits, const float* part_o, const float* part_ml, float* otilde,
+                         float* ml1, hipStream_t st);
 void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
                          const float* part_ml, void* otilde, hipStream_t st);
 

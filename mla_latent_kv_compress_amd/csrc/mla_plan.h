@@ -74,7 +74,7 @@ constexpr int kOrderMax = 2048;
 struct DecodePlan {
   int splits;
   bool ordered;               // rank the sequences by length before the attention (more than one
-                              // round of work-groups on the 64-head kernel)
+                              // round of work-groups on the 64-head kernel, at most 8 splits)
   size_t off_order;           // int32 [B]
   CompressPlan comp;
   QueryPlan q;
@@ -85,7 +85,8 @@ struct DecodePlan {
   size_t off_qhat;            // act  [B][H][W]    absorbed, scaled query
   size_t off_part_o;          // fp32 [B][splits][H][dc]
   size_t off_part_ml;         // fp32 [B][splits][H][2]
-  size_t off_otilde;          // f32 [B][H][dc], or bf16 [B][H][2*dc] = [hi | lo] halves
+  size_t off_otilde;          // f32 [B][H][dc], or bf16 [B][H][2*dc] = [hi | lo] halves (same bytes)
+  size_t off_ml1;             // fp32 [B][H][2]: merged state (0, 1) when the splits are merged first
   size_t bytes;
 };
 int auto_splits(const Dims& d, Path path, int B, int max_blocks);
