@@ -511,6 +511,7 @@ void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st) {
                        static_cast<float*>(a.out));
     return;
   }
+  if (launch_prefill_attn_fa(a, st)) return;
   dim3 grid((a.max_q + 63) / 64, a.H, a.S);
   if (a.out_type == K_BF16)
     hipLaunchKernelGGL(prefill_attn_mfma_kernel<S_BF16>, grid, dim3(256), 0, st, a.H, a.max_ctx, a.cu, a.start,

@@ -121,5 +121,8 @@ struct PrefillAttnArgs {
   void* out;                 // [T][H][dv] out_type
 };
 void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st);
+// Flash-style causal prefill attention (k_prefill.hip), bf16 path with nope 128, rope 64, v 128,
+// d_c 512; false if the shape does not apply.
+bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st);
 
 }  // namespace mla

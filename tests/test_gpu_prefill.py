@@ -56,6 +56,9 @@ CASES = {
     "dsv2_bf16": (DSV2, "bf16", "bf16", [0, 50], [100, 64]),
     "dsv2_fp8": (DSV2, "bf16", "fp8", [0, 130], [70, 33]),
     "lite_bf16": (LITE, "bf16", "bf16", [0, 1], [129, 64]),
+    # several 128-query tiles and 64-key tiles with ragged tails, cached history before the chunk
+    "dsv2_bf16_tiles": (DSV2, "bf16", "bf16", [300, 0, 1000], [300, 257, 130]),
+    "dsv2_fp8_tiles": (DSV2, "bf16", "fp8", [64, 0], [200, 129]),
 }
 
 
@@ -106,19 +109,20 @@ def test_prefill_bf16_output():
         assert all(bf16_out_ok(got[i], ref[i], TOL["bf16"]) for i in range(len(ref)))
 
 
-def test_prefill_causality():
+@pytest.mark.parametrize("shape,act,n,cut", [(TINY, "f32", 80, 50), (DSV2, "bf16", 300, 200)])
+def test_prefill_causality(shape, act, n, cut):
     """Changing later tokens of a chunk leaves earlier rows bit-identical."""
-    log("prefill causality")
-    layer = Layer(TINY, "f32", "f32", seed=9)
-    pf = Prefill(layer, [0], [80], seed=9)
+    log(f"prefill causality ({act})")
+    layer = Layer(shape, act, act, seed=9)
+    pf = Prefill(layer, [0], [n], seed=9)
     out1, _ = pf.run()
     orig = pf.chunk_hidden
 
     def perturbed(s, start, n):
         x = orig(s, start, n).copy()
-        x[50 - start:] += 1.0
+        x[cut - start:] += 1.0
         return x
     pf.chunk_hidden = perturbed
     out2, _ = pf.run()
-    assert np.array_equal(out1[:50], out2[:50])
-    assert not np.allclose(out1[50:], out2[50:])
+    assert np.array_equal(out1[:cut], out2[:cut])
+    assert not np.allclose(out1[cut:], out2[cut:])
