@@ -9,7 +9,10 @@ and the v projection.  Inputs are seeded synthetic data already resident in HBM.
 JSON line with whole-step throughput, the roofline of the dominant kernel (the attention,
 timed with HIP events recorded around it on the library's stream in a second pass over the
 same K steps, since an event record drains the stream and would inflate the throughput pass)
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+and the fp64 CPU oracle timed on a bounded sample of the same workload.  Unless --no-prefill,
+detail.prefill also reports the chunked prefill of the mixed 236B workload (4 x 4096 prompt
+tokens, fp8 cache, chunks of 1024): prompt tokens/s and algorithmic MFMA TFLOP/s against the
+dense bf16 peak.
 """
 import argparse
 import ctypes
@@ -42,7 +45,57 @@ def parse():
                    help="also run one plain 1 GiB device copy (reference for hardware byte counters)")
     p.add_argument("--graph", action="store_true",
                    help="time the step as HIP-graph replays (the attention pass stays eager)")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the chunked-prefill measurement reported under detail.prefill")
     return p.parse_args()
+
+
+def prefill_measure(passes=3):
+    """Chunked prefill of the mixed workload (236B shape, fp8 cache: 4 prompts x 4096 tokens in
+    chunks of 1024, every chunk one mla_prefill call), timed as whole passes over the chunks."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_compress_amd import configs
+    from mla_latent_kv_compress_amd.workload import Layer, PrefillBatch
+
+    wl = configs.WORKLOADS["dsv2_mixed_fp8"]
+    s = wl.shape
+    layer = Layer(s, wl.act_dtype, wl.cache_dtype, out_dtype="bf16")
+    pb = PrefillBatch(layer, wl.prefill_seqs, wl.prefill_len, wl.prefill_chunk)
+    ws = torch.empty(pb.workspace_size(), dtype=torch.uint8, device="cuda")
+    out = None
+
+    def one_pass():
+        nonlocal out
+        for k in range(pb.num_chunks):
+            out = pb.run_chunk(k, workspace=ws, out=out)
+
+    one_pass()                                   # warm-up (also fills the cache once)
+    times = []
+    for _ in range(passes):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        one_pass()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    T, H = wl.prefill_seqs * wl.prefill_len, s.num_heads
+    pairs = wl.prefill_seqs * wl.prefill_len * (wl.prefill_len + 1) / 2      # causal (query, key) pairs
+    flops = {
+        "q_path": 2.0 * T * (s.hidden_size * s.q_lora_rank + s.q_lora_rank * H * s.qk_head_dim),
+        "kv_a": 2.0 * T * s.hidden_size * s.row_width,
+        "kv_b": 2.0 * T * s.kv_lora_rank * H * (s.qk_nope_head_dim + s.v_head_dim),
+        "attention": 2.0 * pairs * H * (s.qk_head_dim + s.v_head_dim),
+    }
+    total = sum(flops.values())
+    return {
+        "workload": f"dsv2_mixed_fp8 prefill: {wl.prefill_seqs} x {wl.prefill_len} tokens in chunks of "
+                    f"{wl.prefill_chunk}, fp8 cache",
+        "ms": t * 1e3, "tokens_per_s": T / t, "passes": passes, "timing": "median of whole passes, synchronized",
+        "alg_tflop": total / 1e12, "alg_tflop_by_part": {k: v / 1e12 for k, v in flops.items()},
+        "mfma_tflops": total / t / 1e12, "mfma_frac": total / t / 1e12 / BF16_PEAK_TFLOPS,
+        "bound": "mfma (bf16)",
+    }
 
 
 class HipEvents:
@@ -255,6 +308,8 @@ def main():
             "setup_s": setup_s,
         },
     }
+    if not args.no_prefill:
+        line["detail"]["prefill"] = prefill_measure()
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

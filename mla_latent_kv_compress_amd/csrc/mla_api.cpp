@@ -245,7 +245,6 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
 
   DecodeAttnArgs a;
   a.B = B; a.H = d.H; a.dc = d.dc; a.dr = d.dr; a.splits = p.splits;
-  a.heads_per_group = decode_heads_per_group(d, path);
   a.qhat = qhat;
   a.cache = cache->data; a.cache_scale = cache->scale;
   a.block_table = block_table; a.max_blocks = max_blocks; a.ctx = context_lens;

@@ -77,7 +77,7 @@ void launch_prefill_prep(int S, int max_q, const int32_t* cu, const int32_t* sta
 // Split-K decode attention over the latent cache (weight-absorbed form).
 //   qhat [B][H][dc+dr] (pre-scaled by sigma*log2 e), partials o [B][S][H][dc], ml [B][S][H][2]
 struct DecodeAttnArgs {
-  int B, H, dc, dr, splits, heads_per_group;
+  int B, H, dc, dr, splits;
   const void* qhat;
   const void* cache; const float* cache_scale;
   const int32_t* block_table; int max_blocks;

@@ -112,14 +112,7 @@ static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q
   q->off_q_acc = q->direct ? 0 : L.take(size_t(q->split_b.n) * T * nq * 4);
 }
 
-int decode_heads_per_group(const Dims& d, Path path) {
-  if (path != PATH_BF16) return 1;
-  // bf16 or fp8 cache: the 64-head split-role kernel, the last group padded when H is not a multiple
-  if ((d.cache_dt == MLA_BF16 || d.cache_dt == MLA_FP8_E4M3) && d.dc == 512 && d.dr == 64) return 64;
-  for (int g = 64; g >= 16; g /= 2)
-    if (d.H % g == 0) return g;
-  return 16;
-}
+int decode_heads_per_group(const Dims&, Path path) { return path == PATH_BF16 ? 64 : 1; }
 
 int auto_splits(const Dims& d, Path path, int B, int max_blocks) {
   const int hpg = decode_heads_per_group(d, path);

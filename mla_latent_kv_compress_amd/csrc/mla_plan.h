@@ -63,9 +63,9 @@ struct QueryPlan {            // q path for T tokens, shared by decode and prefi
   size_t off_q_acc;           // fp32 [split_b.n][T][H*dqk]        (!direct)
 };
 
-// Heads one decode work-group serves (bf16 path): 64 with a bf16 or fp8 cache of 512 + 64 values
-// per row (the last group padded; the head groups of a sequence split stream its rows together),
-// else the largest of 64/32/16 dividing H; 1 on the fp32 path.
+// Heads one decode work-group serves: 64 on the bf16 path (bf16 or fp8 cache; the last group is
+// padded when H is not a multiple; the head groups of a sequence split stream its rows together),
+// 1 on the fp32 path.
 int decode_heads_per_group(const Dims& d, Path path);
 
 // Longest batch for which the 64-head decode kernel takes the sequences longest first.
