@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.cpp", "mla_plan.cpp", "k_gemm.hip", "k_rows.hip", "k_attn.hip", "k_decode.hip", "k_prefill.hip"]
+SOURCES = ["mla_api.cpp", "mla_plan.cpp", "k_gemm.hip", "k_rows.hip", "k_attn.hip", "k_decode.hip", "k_prefill.hip", "k_gemm_tile.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 

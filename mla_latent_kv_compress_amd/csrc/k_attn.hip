@@ -88,6 +88,68 @@ void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t
   launch_decode_attn_v2(cache, a, st);           // every bf16-path shape (d_c 512, d_r 64, H % 16 == 0)
 }
 
+// ==================================================================== prefill, fp32 SIMT
+// Generic dims.  Grid (max_q, H, S); one query per block, 256 threads over keys.
+__global__ __launch_bounds__(256) void prefill_attn_simt_kernel(
+    int H, int dn, int dr, int dv, int dc, int max_ctx, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ start, const float* __restrict__ qs, const float* __restrict__ kv,
+    const float* __restrict__ lat, float* __restrict__ out) {
+  extern __shared__ float sh[];                     // q [dn+dr] | p [256]
+  __shared__ float red[16];
+  const int i = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+  const int q_begin = cu[s], len = cu[s + 1] - q_begin;
+  if (i >= len) return;
+  const int dqk = dn + dr, dkv = dn + dv, W = dc + dr;
+  const int qpos = start[s] + i;
+  float* q = sh;
+  float* pbuf = sh + dqk;
+  for (int k = tid; k < dqk; k += 256) q[k] = qs[(long(q_begin + i) * H + h) * dqk + k];
+  __syncthreads();
+  const long kvb = long(s) * max_ctx;
+  constexpr int KO = 16;                            // dv <= 4096
+  float o[KO];
+#pragma unroll
+  for (int k = 0; k < KO; ++k) o[k] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int tb = 0; tb <= qpos; tb += 256) {
+    const int t = tb + tid;
+    float sc = -INFINITY;
+    if (t <= qpos) {
+      const float* kr = kv + ((kvb + t) * H + h) * dkv;
+      const float* pr = lat + (kvb + t) * W + dc;
+      float acc = 0.f;
+      for (int k = 0; k < dn; ++k) acc = fmaf(q[k], kr[k], acc);
+      for (int k = 0; k < dr; ++k) acc = fmaf(q[dn + k], pr[k], acc);
+      sc = acc;
+    }
+    const float mx = block_max(sc, red);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    const float pv = t <= qpos ? exp2f(sc - m_new) : 0.f;
+    const float ps = block_sum(pv, red);
+    pbuf[tid] = pv;
+    __syncthreads();
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    const int n = min(256, qpos + 1 - tb);
+#pragma unroll
+    for (int k = 0; k < KO; ++k) {
+      const int c = tid + 256 * k;
+      if (c < dv) {
+        float acc = o[k] * alpha;
+        for (int j = 0; j < n; ++j) acc = fmaf(pbuf[j], kv[((kvb + tb + j) * H + h) * dkv + dn + c], acc);
+        o[k] = acc;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < KO; ++k) {
+    const int c = tid + 256 * k;
+    if (c < dv) out[(long(q_begin + i) * H + h) * dv + c] = o[k] / l_run;
+  }
+}
+
 void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st) {
   if (act == K_F32) {
     size_t sh = size_t(a.dn + a.dr + 256) * sizeof(float);

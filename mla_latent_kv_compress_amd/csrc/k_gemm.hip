@@ -868,6 +868,7 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
                          g.ldw, g.sw, static_cast<float*>(g.Y), g.ldc, g.sy, g.ssplit, g.alpha, g.nsplit);
     return;
   }
+  if (launch_gemm_tile(g, st)) return;
   if (g.nn) launch_bf16_out<true>(g, st);
   else launch_bf16_out<false>(g, st);
 }

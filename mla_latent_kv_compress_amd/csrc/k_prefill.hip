@@ -21,6 +21,7 @@
 // Query tiles are dispatched heaviest (latest in the chunk, most keys) first.
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "mla_lds.h"
 
 namespace mla {
 
@@ -34,28 +35,10 @@ constexpr float kLazy = 8.0f;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF));
-}
-
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Direct global->LDS load of 16 bytes per lane (lane i lands at lds + 16 i); untracked by the
-// compiler, awaited with wait_vm before the barrier that publishes the tile.
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
-}
+using lds::barrier;
+using lds::dma16;
+using lds::wait_vm;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return lds::addr(p); }
 
 __device__ __forceinline__ s16x4_t tr_read(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4_t __attribute__((address_space(3)))*)(p));
@@ -196,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
     issue(j + 1);
     if (j + 1 < nt) wait_vm<kLoadsPerWave>();
     else wait_vm<0>();
-    lds_barrier();                                 // tile j in LDS for every wave
+    barrier();                                 // tile j in LDS for every wave
     const char* t = smem + (j & 1) * kTileBytes;
     const int t0 = kKT * j;
 
@@ -262,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
         o[vt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[q >> 1][q & 1], o[vt], 0, 0, 0);
       }
     }
-    lds_barrier();                                 // tile j's buffer free for tile j + 2
+    barrier();                                 // tile j's buffer free for tile j + 2
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -23,6 +23,9 @@ struct GemmArgs {
   float alpha;
 };
 void launch_gemm(const GemmArgs& g, hipStream_t st);
+// 256 x 256-tile GEMM (k_gemm_tile.hip) for large TN products with a bf16 or fp16 output and no K
+// split (the prefill's q_b projection and kv_b decompression); false if the problem does not fit.
+bool launch_gemm_tile(const GemmArgs& g, hipStream_t st);
 // Two independent fp32-output skinny GEMMs in one launch; false (nothing launched) when either
 // does not meet the skinny kernel's conditions.
 bool launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t st);
