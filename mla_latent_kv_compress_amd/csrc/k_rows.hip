@@ -304,6 +304,25 @@ __global__ __launch_bounds__(256) void q_rope_f16_kernel(int H, int dn, int dr, 
   const int t = blockIdx.x, half = dr / 2, dqk = dn + dr;
   for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(pos[t], i, dr, theta, &cs[i], &cs[half + i]);
   __syncthreads();
+  if ((dn | dr) % 8 == 0) {                        // 16-byte pieces: four pairs per thread
+    const int pieces = dr / 8;
+    for (int e = threadIdx.x; e < H * pieces; e += blockDim.x) {
+      const int h = e / pieces, pc = e % pieces;
+      uint4* q = reinterpret_cast<uint4*>(qs + (long(t) * H + h) * dqk + dn + 8 * pc);
+      uint4 v = *q;
+      uint16_t* x = reinterpret_cast<uint16_t*>(&v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pi = 4 * pc + j;
+        const float c = cs[pi], s = cs[half + pi];
+        const float ev = h2f(x[2 * j]), ov = h2f(x[2 * j + 1]);
+        x[2 * j] = f2h(ev * c - ov * s);
+        x[2 * j + 1] = f2h(ev * s + ov * c);
+      }
+      *q = v;
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
     const int h = e / half, pi = e % half;
     const float c = cs[pi], s = cs[half + pi];
