@@ -87,6 +87,21 @@ typedef struct mla_config {
   int32_t out_dtype;         /* MLA_F32 or MLA_BF16 (MLA_BF16 needs act_dtype MLA_BF16): the
                                 attention output.  A bf16 output carries its own rounding of up
                                 to 2^-8 of each value on top of the computation's error. */
+  /* RoPE context extension by frequency interpolation (YaRN), page "MLA 的两个核心部件" /
+   * opening section: the 128K context comes from YaRN scaling of the rotary embedding; the page
+   * gives no constants, so they are the caller's.  With rope_factor <= 1 (0 included) the
+   * rotation is the plain one.  With rope_factor = s > 1, pair i of frequency f_i turns
+   * r_i = rope_original_max_position * f_i / (2 pi) times over the original context and uses
+   *   f_i                      if r_i >= rope_beta_fast,
+   *   f_i / s                  if r_i <= rope_beta_slow,
+   *   (1 - g) f_i / s + g f_i  with g = (r_i - rope_beta_slow) / (rope_beta_fast - rope_beta_slow)
+   * in between.  rope_mscale (0: 1) multiplies cos and sin of every rotation, of q_pe and k_pe
+   * alike; a temperature on all scores goes in softmax_scale. */
+  float rope_factor;
+  int32_t rope_original_max_position;  /* > 0 when rope_factor > 1 */
+  float rope_beta_fast;                /* > rope_beta_slow when rope_factor > 1 */
+  float rope_beta_slow;                /* >= 0 */
+  float rope_mscale;
 } mla_config;
 
 /* Weight pointers (device, act_dtype).  With q_lora_rank == 0, q_b_proj is q_proj

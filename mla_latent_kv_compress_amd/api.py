@@ -31,7 +31,10 @@ class MlaConfig(ctypes.Structure):
                 ("v_head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("softmax_scale", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("cache_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("cache_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("rope_factor", ctypes.c_float), ("rope_original_max_position", ctypes.c_int32),
+                ("rope_beta_fast", ctypes.c_float), ("rope_beta_slow", ctypes.c_float),
+                ("rope_mscale", ctypes.c_float)]
 
 
 class MlaWeights(ctypes.Structure):
@@ -93,7 +96,9 @@ def make_config(shape, act_dtype, cache_dtype, out_dtype="f32"):
     return MlaConfig(shape.hidden_size, shape.num_heads, shape.q_lora_rank, shape.kv_lora_rank,
                      shape.qk_nope_head_dim, shape.qk_rope_head_dim, shape.v_head_dim, PAGE_SIZE,
                      shape.rope_theta, shape.rms_eps, shape.softmax_scale,
-                     DTYPE_CODES[act_dtype], DTYPE_CODES[cache_dtype], DTYPE_CODES[out_dtype])
+                     DTYPE_CODES[act_dtype], DTYPE_CODES[cache_dtype], DTYPE_CODES[out_dtype],
+                     shape.rope_factor, shape.rope_original_max_position, shape.rope_beta_fast,
+                     shape.rope_beta_slow, shape.rope_mscale)
 
 
 TORCH_OUT = {0: torch.float32, 1: torch.bfloat16}

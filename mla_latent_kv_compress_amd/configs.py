@@ -23,6 +23,13 @@ class LayerShape:
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
     softmax_scale: float = 0.0    # 0: 1/sqrt(qk_nope_head_dim + qk_rope_head_dim)
+    # YaRN frequency interpolation of the rotary embedding (rope_factor <= 1: off); the pages give
+    # no constants, so none of the workloads uses it
+    rope_factor: float = 0.0
+    rope_original_max_position: int = 0
+    rope_beta_fast: float = 0.0
+    rope_beta_slow: float = 0.0
+    rope_mscale: float = 0.0
 
     @property
     def row_width(self):

@@ -5,8 +5,8 @@
 // [32w, 32w + 32) of the tile.  Keys and values stream through LDS in tiles of 64 keys (k_nope
 // 16 KiB | k_pe 8 KiB | v 16 KiB), double-buffered with direct global->LDS loads, so two
 // work-groups (80 KiB each) share a CU.  Per tile and wave:
-//   S^T[key][query] = K . Q^T with v_mfma_f32_32x32x16 (k_nope in fp16, k_pe in bf16 as cached,
-//   the query in registers: 8 fp16 + 4 bf16 K steps per 32-key sub-tile);
+//   S^T[key][query] = K . Q^T with v_mfma_f32_32x32x16_f16 (k_nope from the decompression, k_pe
+//   from an fp16 copy the gather writes, the query in registers: 12 K steps per 32-key sub-tile);
 //   online softmax per query in base 2 (queries are pre-scaled by sigma * log2 e), with the
 //   running max moved only when a tile's max passes it by more than kLazy (p <= 2^kLazy, far
 //   inside fp16), so the output accumulators are rescaled only then;
@@ -51,7 +51,7 @@ __device__ __forceinline__ f16x8_t join_f16(s16x4_t lo, s16x4_t hi) {
 }
 
 // Load k of wave w: instruction i = w + 4k of the tile.  Returns the byte offset, relative to
-// the tile's base (kv for k_nope and v, lat + 1024 for k_pe), of the 16 bytes lane `lane`
+// the tile's base (kv for k_nope and v, the fp16 k_pe copy for k_pe), of the 16 bytes lane `lane`
 // fetches, rows at or beyond `valid` re-reading row valid - 1; `row_bytes` is H * 512 (one key's
 // k_nope | v of all heads).
 __device__ __forceinline__ uint32_t load_offset(int k, int wave, int lane, int valid, uint32_t row_bytes) {
@@ -64,7 +64,7 @@ __device__ __forceinline__ uint32_t load_offset(int k, int wave, int lane, int v
   } else if (i < 24) {                         // k_pe: 8 rows of 128 B per KiB
     row = 8 * (i - 16) + (lane >> 3);
     c = (lane & 7) ^ ((row >> 1) & 7);
-    stride = 1152;
+    stride = 128;
   } else {                                     // v: 4 rows of 256 B per KiB
     row = 4 * (i - 24) + (lane >> 4);
     c = (lane & 15) ^ (2 * (row & 7));
@@ -84,7 +84,7 @@ __device__ __forceinline__ int load_lds_offset(int k, int wave) {
 template <int OUT>
 __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
     int H, int S, int nqt, int max_ctx, const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
-    const uint16_t* __restrict__ qs, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ lat,
+    const uint16_t* __restrict__ qs, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ kpe,
     typename StoreT<OUT>::type* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -103,22 +103,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
   const int wave_qmin = st0 + qt * kQT + 32 * wave;
   const uint32_t row_bytes = uint32_t(H) * 512u;
   const char* kvc = reinterpret_cast<const char*>(kv) + (long(s) * max_ctx * H + h) * 512;
-  const char* latc = reinterpret_cast<const char*>(lat) + long(s) * max_ctx * 1152 + 1024;
+  const char* kpec = reinterpret_cast<const char*>(kpe) + long(s) * max_ctx * 128;
 
-  // Query fragments (B operand): Q[query ql][16 st + 8 e .. +7]; the RoPE part converted to bf16.
-  f16x8_t qn[8];
-  bf16x8_t qr[4];
+  // Query fragments (B operand): Q[query ql][16 st + 8 e .. +7].
+  f16x8_t qn[8], qr[4];
   {
     const _Float16* qp =
         reinterpret_cast<const _Float16*>(qs) + (long(q_begin + min(qi, len - 1)) * H + h) * 192 + 8 * e;
 #pragma unroll
     for (int st = 0; st < 8; ++st) qn[st] = *reinterpret_cast<const f16x8_t*>(qp + 16 * st);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const f16x8_t x = *reinterpret_cast<const f16x8_t*>(qp + 128 + 16 * st);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qr[st][j] = (__bf16)float(x[j]);
-    }
+    for (int st = 0; st < 4; ++st) qr[st] = *reinterpret_cast<const f16x8_t*>(qp + 128 + 16 * st);
   }
 
   uint32_t full_off[kLoadsPerWave];
@@ -128,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
     if (j >= nt) return;
     char* dst = smem + (j & 1) * kTileBytes;
     const char* kvb = kvc + long(kKT * j) * row_bytes;
-    const char* lb = latc + long(kKT * j) * 1152;
+    const char* lb = kpec + long(kKT * j) * 128;
     const int valid = min(kKT, ctx - kKT * j);
     if (valid == kKT) {
 #pragma unroll
@@ -151,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
     return *reinterpret_cast<const f16x8_t*>(t + n_row + 8192 * u + 16 * ((2 * st + e) ^ n_x));
   };
   auto pe_a = [&](const char* t, int u, int st) {
-    return *reinterpret_cast<const bf16x8_t*>(t + p_row + 4096 * u + 16 * ((2 * st + e) ^ p_x));
+    return *reinterpret_cast<const f16x8_t*>(t + p_row + 4096 * u + 16 * ((2 * st + e) ^ p_x));
   };
   // V^T reads: lane i of each 16-lane group supplies key row T + (i >> 2), v column
   // c0 + 4 (i & 3), c0 = 32 vt + 16 ((lane >> 4) & 1); T = 16 q + 4 e (and + 8 for the second read).
@@ -195,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pe_a(t, u, st), qr[st], sc[u], 0, 0, 0);
+      for (int u = 0; u < 2; ++u) sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pe_a(t, u, st), qr[st], sc[u], 0, 0, 0);
 
     // Causal mask (only where some key of the tile passes some query of the wave) and the
     // tile max per query (the lane and its partner lane ^ 32 hold the query's 64 keys).
@@ -267,11 +262,11 @@ bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st) {
   if (a.out_type == K_BF16)
     hipLaunchKernelGGL(prefill_attn_fa_kernel<S_BF16>, grid, dim3(256), 0, st, a.H, a.S, nqt, a.max_ctx, a.cu,
                        a.start, static_cast<const uint16_t*>(a.qs), static_cast<const uint16_t*>(a.kv),
-                       static_cast<const uint16_t*>(a.lat), static_cast<uint16_t*>(a.out));
+                       static_cast<const uint16_t*>(a.kpe), static_cast<uint16_t*>(a.out));
   else
     hipLaunchKernelGGL(prefill_attn_fa_kernel<S_F32>, grid, dim3(256), 0, st, a.H, a.S, nqt, a.max_ctx, a.cu,
                        a.start, static_cast<const uint16_t*>(a.qs), static_cast<const uint16_t*>(a.kv),
-                       static_cast<const uint16_t*>(a.lat), static_cast<float*>(a.out));
+                       static_cast<const uint16_t*>(a.kpe), static_cast<float*>(a.out));
   return true;
 }
 

@@ -49,7 +49,7 @@ template <typename ActT, int CACHE>
 __device__ __forceinline__ void compress_row(
     int t, int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
     const int32_t* __restrict__ pos, const int64_t* __restrict__ slots, void* __restrict__ cache,
-    float* __restrict__ cache_scale, long num_slots, float eps, float theta, float* __restrict__ rope_tab,
+    float* __restrict__ cache_scale, long num_slots, float eps, RopeParams rp, float* __restrict__ rope_tab,
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks, float* row, float* red) {
   const int W = dc + dr;
   // Decode (ctx given): the token is the last of a context of ctx[t] rows, at position ctx[t] - 1.
@@ -70,7 +70,7 @@ __device__ __forceinline__ void compress_row(
   const int ri = int(threadIdx.x) - (int(blockDim.x) - dr / 2);
   float rc = 1.f, rsn = 0.f;
   if (ri >= 0) {
-    rope_cs(p, ri, dr, theta, &rc, &rsn);
+    rope_cs(p, ri, dr, rp, &rc, &rsn);
     if (rope_tab) {
       rope_tab[long(t) * dr + ri] = rc;
       rope_tab[long(t) * dr + dr / 2 + ri] = rsn;
@@ -116,25 +116,25 @@ template <typename ActT, int CACHE>
 __global__ __launch_bounds__(256) void compress_rows_kernel(
     int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
     const int32_t* __restrict__ pos, const int64_t* __restrict__ slots, void* __restrict__ cache,
-    float* __restrict__ cache_scale, long num_slots, float eps, float theta, float* __restrict__ rope_tab,
+    float* __restrict__ cache_scale, long num_slots, float eps, RopeParams rp, float* __restrict__ rope_tab,
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks) {
   extern __shared__ float row[];                    // [dc + dr]
   __shared__ float red[16];
   compress_row<ActT, CACHE>(blockIdx.x, dc, dr, T, nsplit, acc, gamma, pos, slots, cache, cache_scale, num_slots,
-                            eps, theta, rope_tab, ctx, bt, max_blocks, row, red);
+                            eps, rp, rope_tab, ctx, bt, max_blocks, row, red);
 }
 
 void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit, const float* acc,
                           const void* gamma, const int32_t* pos, const int64_t* slots,
                           void* cache_data, float* cache_scale, long num_slots, float eps,
-                          float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                          const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
                           hipStream_t st) {
   if (T <= 0) return;
   size_t sh = size_t(dc + dr) * sizeof(float);
 #define MLA_CR(A, C)                                                                          \
   hipLaunchKernelGGL((compress_rows_kernel<A, C>), dim3(T), dim3(256), sh, st, dc, dr, T, nsplit, \
                      acc, static_cast<const A*>(gamma), pos, slots, cache_data, cache_scale,      \
-                     num_slots, eps, theta, rope_tab, ctx, bt, max_blocks)
+                     num_slots, eps, rp, rope_tab, ctx, bt, max_blocks)
   if (act == K_F32) {
     MLA_CR(float, K_F32);
   } else if (cache == K_BF16) {
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsp
 template <typename ActT, int CACHE>
 __global__ __launch_bounds__(256) void decode_rows_kernel(
     int dc, int dr, int T, int nsplit_kv, const float* __restrict__ acc_kv, const ActT* __restrict__ gamma_kv,
-    void* __restrict__ cache, float* __restrict__ cache_scale, long num_slots, float eps, float theta,
+    void* __restrict__ cache, float* __restrict__ cache_scale, long num_slots, float eps, RopeParams rp,
     float* __restrict__ rope_tab, const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks,
     int nq, int nsplit_q, const float* __restrict__ acc_q, const ActT* __restrict__ gamma_q, ActT* __restrict__ cq) {
   extern __shared__ float row[];                    // [max(dc + dr, nq)]
@@ -193,21 +193,21 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(
   const int t = blockIdx.x;
   if (t < T)
     compress_row<ActT, CACHE>(t, dc, dr, T, nsplit_kv, acc_kv, gamma_kv, nullptr, nullptr, cache, cache_scale,
-                              num_slots, eps, theta, rope_tab, ctx, bt, max_blocks, row, red);
+                              num_slots, eps, rp, rope_tab, ctx, bt, max_blocks, row, red);
   else
     rmsnorm_row<ActT>(t - T, T, nq, nsplit_q, acc_q, gamma_q, cq, eps, row, red);
 }
 
 bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
                         const void* gamma_kv, void* cache_data, float* cache_scale, long num_slots, float eps,
-                        float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                        const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
                         int nq, int nsplit_q, const float* acc_q, const void* gamma_q, void* cq, hipStream_t st) {
   if (T <= 0 || act != K_BF16 || (cache != K_BF16 && cache != K_FP8) || !ctx || !rope_tab) return false;
   const size_t sh = size_t(max(dc + dr, nq)) * sizeof(float);
 #define MLA_DR(C)                                                                                     \
   hipLaunchKernelGGL((decode_rows_kernel<uint16_t, C>), dim3(2 * T), dim3(256), sh, st, dc, dr, T, nsplit_kv, \
                      acc_kv, static_cast<const uint16_t*>(gamma_kv), cache_data, cache_scale, num_slots, eps, \
-                     theta, rope_tab, ctx, bt, max_blocks, nq, nsplit_q, acc_q,                        \
+                     rp, rope_tab, ctx, bt, max_blocks, nq, nsplit_q, acc_q,                        \
                      static_cast<const uint16_t*>(gamma_q), static_cast<uint16_t*>(cq))
   if (cache == K_BF16)
     MLA_DR(K_BF16);
@@ -238,7 +238,7 @@ constexpr int kQH = 4;
 template <int ACT, int QS>
 __global__ __launch_bounds__(256) void q_pack_kernel(bool absorbed, int T, int H, int dn, int dr, int dc,
                                                      int nsplit, const float* __restrict__ q_acc,
-                                                     const int32_t* __restrict__ pos, float scale, float theta,
+                                                     const int32_t* __restrict__ pos, float scale, RopeParams rp,
                                                      typename StoreT<ACT>::type* __restrict__ qnope,
                                                      typename StoreT<ACT>::type* __restrict__ qhat,
                                                      typename StoreT<QS>::type* __restrict__ qs) {
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void q_pack_kernel(bool absorbed, int T, int H
   const long nq = long(H) * dqk;
   const int per_head = dn + half;
   const int nh = min(kQH, H - h_lo);
-  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(pos[t], i, dr, theta, &cs[i], &cs[half + i]);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(pos[t], i, dr, rp, &cs[i], &cs[half + i]);
   __syncthreads();
   auto q_at = [&](long j) -> float { return split_sum(q_acc, nsplit, long(T) * nq, long(t) * nq + j); };
   for (int e = threadIdx.x; e < nh * per_head; e += blockDim.x) {
@@ -277,32 +277,32 @@ __global__ __launch_bounds__(256) void q_pack_kernel(bool absorbed, int T, int H
 }
 
 void launch_q_pack(int act, int qs_type, bool absorbed, int T, int H, int dn, int dr, int dc, int nsplit,
-                   const float* q_acc, const int32_t* pos, float scale, float theta, void* qnope, void* qhat,
+                   const float* q_acc, const int32_t* pos, float scale, const RopeParams& rp, void* qnope, void* qhat,
                    void* qs, hipStream_t st) {
   if (T <= 0) return;
   dim3 grid(T, (H + kQH - 1) / kQH);
   size_t sh = size_t(dr) * sizeof(float);
   if (act == K_F32)
     hipLaunchKernelGGL((q_pack_kernel<S_F32, S_F32>), grid, dim3(256), sh, st, absorbed, T, H, dn, dr, dc,
-                       nsplit, q_acc, pos, scale, theta, static_cast<float*>(qnope), static_cast<float*>(qhat),
+                       nsplit, q_acc, pos, scale, rp, static_cast<float*>(qnope), static_cast<float*>(qhat),
                        static_cast<float*>(qs));
   else if (qs_type == K_F16)
     hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_F16>), grid, dim3(256), sh, st, absorbed, T, H, dn, dr, dc,
-                       nsplit, q_acc, pos, scale, theta, static_cast<uint16_t*>(qnope),
+                       nsplit, q_acc, pos, scale, rp, static_cast<uint16_t*>(qnope),
                        static_cast<uint16_t*>(qhat), static_cast<uint16_t*>(qs));
   else
     hipLaunchKernelGGL((q_pack_kernel<S_BF16, S_BF16>), grid, dim3(256), sh, st, absorbed, T, H, dn, dr, dc,
-                       nsplit, q_acc, pos, scale, theta, static_cast<uint16_t*>(qnope),
+                       nsplit, q_acc, pos, scale, rp, static_cast<uint16_t*>(qnope),
                        static_cast<uint16_t*>(qhat), static_cast<uint16_t*>(qs));
 }
 
 // In-place RoPE of the q_pe part of fp16 queries (the projection already wrote them scaled).
 // Block per token; the token's angles are formed once in shared memory.
 __global__ __launch_bounds__(256) void q_rope_f16_kernel(int H, int dn, int dr, const int32_t* __restrict__ pos,
-                                                         float theta, uint16_t* __restrict__ qs) {
+                                                         RopeParams rp, uint16_t* __restrict__ qs) {
   extern __shared__ float cs[];
   const int t = blockIdx.x, half = dr / 2, dqk = dn + dr;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(pos[t], i, dr, theta, &cs[i], &cs[half + i]);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(pos[t], i, dr, rp, &cs[i], &cs[half + i]);
   __syncthreads();
   if ((dn | dr) % 8 == 0) {                        // 16-byte pieces: four pairs per thread
     const int pieces = dr / 8;
@@ -333,9 +333,10 @@ __global__ __launch_bounds__(256) void q_rope_f16_kernel(int H, int dn, int dr, 
   }
 }
 
-void launch_q_rope_f16(int T, int H, int dn, int dr, const int32_t* pos, float theta, void* qs, hipStream_t st) {
+void launch_q_rope_f16(int T, int H, int dn, int dr, const int32_t* pos, const RopeParams& rp, void* qs,
+                       hipStream_t st) {
   if (T <= 0) return;
-  hipLaunchKernelGGL(q_rope_f16_kernel, dim3(T), dim3(256), size_t(dr) * sizeof(float), st, H, dn, dr, pos, theta,
+  hipLaunchKernelGGL(q_rope_f16_kernel, dim3(T), dim3(256), size_t(dr) * sizeof(float), st, H, dn, dr, pos, rp,
                      static_cast<uint16_t*>(qs));
 }
 
@@ -493,40 +494,42 @@ void launch_decode_merge(int act, int B, int H, int dc, int splits, const float*
 // ------------------------------------------------------------------ prefill gather
 // lat[s][t][:] = dequantised cache row of position t of sequence s, t < ctx_s; zero beyond.
 template <typename ActT, int CACHE>
-__global__ __launch_bounds__(256) void gather_rows_kernel(int max_ctx, int W, const int32_t* __restrict__ cu,
+__global__ __launch_bounds__(256) void gather_rows_kernel(int max_ctx, int W, int dc, const int32_t* __restrict__ cu,
                                                           const int32_t* __restrict__ start,
                                                           const int32_t* __restrict__ bt, int max_blocks,
                                                           const void* __restrict__ cache,
                                                           const float* __restrict__ cache_scale,
-                                                          ActT* __restrict__ lat) {
+                                                          ActT* __restrict__ lat, uint16_t* __restrict__ kpe16) {
   const int s = blockIdx.y, t = blockIdx.x;
   const int ctx = start[s] + (cu[s + 1] - cu[s]);
-  ActT* dst = lat + (long(s) * max_ctx + t) * W;
+  const long row = long(s) * max_ctx + t;
+  ActT* dst = lat + row * W;
+  uint16_t* pe = kpe16 ? kpe16 + row * (W - dc) : nullptr;          // pe[i - dc], i in [dc, W)
   if (t >= ctx) {
-    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, 0.f);
+    for (int i = threadIdx.x; i < W; i += blockDim.x) {
+      stf<ActT>(dst, i, 0.f);
+      if (pe && i >= dc) pe[i - dc] = f2h(0.f);
+    }
     return;
   }
   const long slot = long(bt[long(s) * max_blocks + t / kPage]) * kPage + t % kPage;
-  if (CACHE == K_F32) {
-    const float* src = static_cast<const float*>(cache) + slot * W;
-    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, src[i]);
-  } else if (CACHE == K_BF16) {
-    const uint16_t* src = static_cast<const uint16_t*>(cache) + slot * W;
-    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, bf2f(src[i]));
-  } else {
-    const uint8_t* src = static_cast<const uint8_t*>(cache) + slot * W;
-    const float sc = cache_scale[slot];
-    for (int i = threadIdx.x; i < W; i += blockDim.x) stf<ActT>(dst, i, sc * e4m3_to_f(src[i]));
+  for (int i = threadIdx.x; i < W; i += blockDim.x) {
+    float v;
+    if (CACHE == K_F32) v = static_cast<const float*>(cache)[slot * W + i];
+    else if (CACHE == K_BF16) v = bf2f(static_cast<const uint16_t*>(cache)[slot * W + i]);
+    else v = cache_scale[slot] * e4m3_to_f(static_cast<const uint8_t*>(cache)[slot * W + i]);
+    stf<ActT>(dst, i, v);
+    if (pe && i >= dc) pe[i - dc] = f2h(v);
   }
 }
 
-void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, const int32_t* cu,
+void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, int dc, const int32_t* cu,
                         const int32_t* start, const int32_t* bt, int max_blocks, const void* cache_data,
-                        const float* cache_scale, void* lat, hipStream_t st) {
+                        const float* cache_scale, void* lat, void* kpe16, hipStream_t st) {
   dim3 grid(max_ctx, S);
-#define MLA_GR(A, C)                                                                             \
-  hipLaunchKernelGGL((gather_rows_kernel<A, C>), grid, dim3(256), 0, st, max_ctx, W, cu, start, bt, \
-                     max_blocks, cache_data, cache_scale, static_cast<A*>(lat))
+#define MLA_GR(A, C)                                                                                 \
+  hipLaunchKernelGGL((gather_rows_kernel<A, C>), grid, dim3(256), 0, st, max_ctx, W, dc, cu, start, bt, \
+                     max_blocks, cache_data, cache_scale, static_cast<A*>(lat), static_cast<uint16_t*>(kpe16))
   if (act == K_F32) {
     MLA_GR(float, K_F32);
   } else if (cache == K_BF16) {

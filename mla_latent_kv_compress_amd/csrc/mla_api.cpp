@@ -49,7 +49,7 @@ void enqueue_compress(const Dims& d, Path path, const mla_config* cfg, const mla
                    acc, d.W(), 0), s);
   launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), T, d.dc, d.dr, cp.split.n, acc,
                        w->kv_a_norm, pos, slots, cache->data, cache->scale,
-                       long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.theta, rope_tab, ctx, bt, max_blocks, s);
+                       long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.rope, rope_tab, ctx, bt, max_blocks, s);
 }
 
 // Query projection of T tokens.  Leaves fp32 partials at q.off_q_acc, or (q.direct) the scaled
@@ -97,10 +97,10 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
   if (!launch_gemm_pair(g_q, g_kv, s)) return false;
   const long num_slots = long(cache->num_blocks) * MLA_PAGE_SIZE;
   if (!launch_decode_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
-                          w->kv_a_norm, cache->data, cache->scale, num_slots, d.eps, d.theta, rope, ctx, bt,
+                          w->kv_a_norm, cache->data, cache->scale, num_slots, d.eps, d.rope, rope, ctx, bt,
                           max_blocks, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, s)) {
     launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
-                         w->kv_a_norm, nullptr, nullptr, cache->data, cache->scale, num_slots, d.eps, d.theta, rope,
+                         w->kv_a_norm, nullptr, nullptr, cache->data, cache->scale, num_slots, d.eps, d.rope, rope,
                          ctx, bt, max_blocks, s);
     launch_rmsnorm_rows(kdt(cfg->act_dtype), B, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, d.eps, s);
   }
@@ -237,7 +237,7 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
                                                 w->kv_b_proj, qhat, s, qn16, qpe32))) {
     if (qsplit) return MLA_ERR_UNSUPPORTED;       // (cannot happen: both need dn 128, dr 64, dc 512)
     if (path == PATH_BF16) launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
-    launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n, qacc, pos, qscale, d.theta, qnope, qhat,
+    launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n, qacc, pos, qscale, d.rope, qnope, qhat,
                   nullptr, s);
     launch_gemm(gemm(path, true, act, B, d.dc, d.dn, whole(d.dn), d.H, qnope, long(d.H) * d.dn, d.dn,
                      w->kv_b_proj, d.dc, long(d.dkv()) * d.dc, qhat, long(d.H) * d.W(), d.W()), s);
@@ -322,14 +322,15 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
   const int qs_type = path == PATH_F32 ? K_F32 : K_F16;
   enqueue_query(d, path, cfg, w, hidden, T, p.q, workspace, qs, qscale, s);
   if (p.q.direct)
-    launch_q_rope_f16(T, d.H, d.dn, d.dr, pos, d.theta, qs, s);
+    launch_q_rope_f16(T, d.H, d.dn, d.dr, pos, d.rope, qs, s);
   else
     launch_q_pack(act, qs_type, false, T, d.H, d.dn, d.dr, d.dc, p.q.split_b.n,
-                  reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)), pos, qscale, d.theta, nullptr,
+                  reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)), pos, qscale, d.rope, nullptr,
                   nullptr, qs, s);
   void* lat = at(workspace, p.off_lat);
-  launch_gather_rows(act, kdt(cfg->cache_dtype), S, max_ctx, d.W(), cu_seqlens, start_pos, block_table,
-                     max_blocks, cache->data, cache->scale, lat, s);
+  void* kpe = path == PATH_BF16 ? at(workspace, p.off_kpe) : nullptr;
+  launch_gather_rows(act, kdt(cfg->cache_dtype), S, max_ctx, d.W(), d.dc, cu_seqlens, start_pos, block_table,
+                     max_blocks, cache->data, cache->scale, lat, kpe, s);
   // Decompress every context latent: kv[s][t] = kv_b_proj . latent -> per head [k_nope | v].
   void* kv = at(workspace, p.off_kv);
   const long nkv = long(d.H) * d.dkv();
@@ -339,7 +340,7 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
   a.S = S; a.H = d.H; a.dn = d.dn; a.dr = d.dr; a.dv = d.dv; a.dc = d.dc;
   a.max_q = max_q_len; a.max_ctx = max_ctx; a.out_type = kdt(cfg->out_dtype);
   a.cu = cu_seqlens; a.start = start_pos;
-  a.qs = qs; a.kv = kv; a.lat = lat; a.out = out;
+  a.qs = qs; a.kv = kv; a.lat = lat; a.kpe = kpe; a.out = out;
   launch_prefill_attn(act, a, s);
   return finish();
 }

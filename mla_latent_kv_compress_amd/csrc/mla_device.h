@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla_rope.h"
+
 namespace mla {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -105,12 +107,20 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return s;
 }
 
-// RoPE angle of pair i (of a d_r-wide vector) at position pos, formed in double precision.
-__device__ __forceinline__ void rope_cs(int pos, int i, int dr, float theta, float* c, float* s) {
-  double freq = pow(double(theta), -2.0 * double(i) / double(dr));
-  double ang = double(pos) * freq;
-  *c = float(cos(ang));
-  *s = float(sin(ang));
+// RoPE of pair i (of a d_r-wide vector) at position pos: cos and sin of its angle, formed in
+// double precision, times mscale.  Frequencies as described with RopeParams (YaRN when
+// factor > 1, after the YaRN paper's interpolation by parts).
+__device__ __forceinline__ void rope_cs(int pos, int i, int dr, const RopeParams& rp, float* c, float* s) {
+  double freq = pow(double(rp.theta), -2.0 * double(i) / double(dr));
+  if (rp.factor > 1.f) {
+    const double turns = double(rp.orig) * freq / (2.0 * 3.14159265358979323846);
+    double g = (turns - double(rp.beta_slow)) / (double(rp.beta_fast) - double(rp.beta_slow));
+    g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+    freq = (1.0 - g) * freq / double(rp.factor) + g * freq;
+  }
+  const double ang = double(pos) * freq;
+  *c = float(cos(ang) * double(rp.mscale));
+  *s = float(sin(ang) * double(rp.mscale));
 }
 
 }  // namespace mla

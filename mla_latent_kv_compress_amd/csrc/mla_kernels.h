@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla_rope.h"
+
 namespace mla {
 
 enum GemmKind { GEMM_F32 = 0, GEMM_BF16 = 1 };
@@ -37,7 +39,7 @@ enum { K_F32 = 0, K_BF16 = 1, K_FP8 = 2, K_F16 = 3 };
 void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit, const float* acc,
                           const void* gamma, const int32_t* pos, const int64_t* slots,
                           void* cache_data, float* cache_scale, long num_slots, float eps,
-                          float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                          const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
                           hipStream_t st);
 // Decode queries on the bf16 path, from the fp32 query projection q ([nsplit][B][H][dn + dr]):
 // qhat[b][h] = [ W_UK^h^T bf16(scale q_nope) | bf16(scale RoPE(q_pe)) ] (bf16), with the
@@ -57,7 +59,7 @@ void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, co
 // table written) and the query-latent RMSNorm in one launch of 2T blocks; false if unsupported.
 bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
                         const void* gamma_kv, void* cache_data, float* cache_scale, long num_slots, float eps,
-                        float theta, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
+                        const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
                         int nq, int nsplit_q, const float* acc_q, const void* gamma_q, void* cq, hipStream_t st);
 
 // Query packing from fp32 partials q_acc [nsplit][T][H*(dn+dr)]: sum, scale by `scale`,
@@ -65,10 +67,10 @@ bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv
 //   absorbed: q_nope -> qnope[t][h][dn]; rotated q_pe -> qhat[t][h][dc + i]  (act dtype)
 //   explicit: [q_nope | rotated q_pe] -> qs[t][h][dn + dr]                   (qs_type)
 void launch_q_pack(int act, int qs_type, bool absorbed, int T, int H, int dn, int dr, int dc,
-                   int nsplit, const float* q_acc, const int32_t* pos, float scale, float theta,
+                   int nsplit, const float* q_acc, const int32_t* pos, float scale, const RopeParams& rp,
                    void* qnope, void* qhat, void* qs, hipStream_t st);
 // RoPE in place on the q_pe part of fp16 queries qs[t][h][dn + dr] (already scaled).
-void launch_q_rope_f16(int T, int H, int dn, int dr, const int32_t* pos, float theta, void* qs,
+void launch_q_rope_f16(int T, int H, int dn, int dr, const int32_t* pos, const RopeParams& rp, void* qs,
                        hipStream_t st);
 
 void launch_decode_prep(int B, const int32_t* ctx, const int32_t* bt, int max_blocks,
@@ -108,10 +110,11 @@ void launch_merge_splits(int B, int H, int dc, int splits, const float* part_o, 
 void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
                          const float* part_ml, void* otilde, hipStream_t st);
 
-// Prefill: gather (and dequantise) each sequence's cached rows [0, ctx) into lat [S][max_ctx][W].
-void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, const int32_t* cu,
+// Prefill: gather (and dequantise) each sequence's cached rows [0, ctx) into lat [S][max_ctx][W];
+// with kpe16 also their k_pe part (columns [dc, W)) in fp16 into kpe16 [S][max_ctx][W - dc].
+void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, int dc, const int32_t* cu,
                         const int32_t* start, const int32_t* bt, int max_blocks,
-                        const void* cache_data, const float* cache_scale, void* lat,
+                        const void* cache_data, const float* cache_scale, void* lat, void* kpe16,
                         hipStream_t st);
 
 // Causal attention of packed chunk queries against decompressed keys / values.
@@ -121,6 +124,7 @@ struct PrefillAttnArgs {
   const void* qs;            // [T][H][dn+dr], pre-scaled by sigma*log2 e (fp16 on the bf16 path)
   const void* kv;            // [S][max_ctx][H][dn+dv]  (fp16 on the bf16 path)
   const void* lat;           // [S][max_ctx][dc+dr] act dtype (k_pe at column dc)
+  const void* kpe;           // [S][max_ctx][dr] fp16 copy of k_pe (bf16 path)
   void* out;                 // [T][H][dv] out_type
 };
 void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st);

@@ -39,6 +39,12 @@ int check_config(const mla_config* cfg, Dims* d, Path* path) {
   if (!(c.rope_theta > 0.f) || !std::isfinite(c.rope_theta)) return MLA_ERR_INVALID_ARG;
   if (!(c.rms_eps >= 0.f) || !std::isfinite(c.rms_eps)) return MLA_ERR_INVALID_ARG;
   if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(c.rope_factor) || !std::isfinite(c.rope_mscale) || c.rope_mscale < 0.f)
+    return MLA_ERR_INVALID_ARG;
+  if (c.rope_factor > 1.f &&
+      (c.rope_original_max_position <= 0 || !std::isfinite(c.rope_beta_fast) || !std::isfinite(c.rope_beta_slow) ||
+       !(c.rope_beta_slow >= 0.f) || !(c.rope_beta_fast > c.rope_beta_slow)))
+    return MLA_ERR_INVALID_ARG;
   if (c.act_dtype != MLA_F32 && c.act_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
   if (dtype_size(c.cache_dtype) == 0) return MLA_ERR_INVALID_ARG;
   if (c.out_dtype != MLA_F32 && c.out_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
@@ -46,7 +52,13 @@ int check_config(const mla_config* cfg, Dims* d, Path* path) {
   Dims dd;
   dd.D = c.hidden_size; dd.H = c.num_heads; dd.dq = c.q_lora_rank; dd.dc = c.kv_lora_rank;
   dd.dn = c.qk_nope_head_dim; dd.dr = c.qk_rope_head_dim; dd.dv = c.v_head_dim;
-  dd.theta = c.rope_theta; dd.eps = c.rms_eps;
+  dd.rope.theta = c.rope_theta;
+  dd.rope.factor = c.rope_factor > 1.f ? c.rope_factor : 1.f;
+  dd.rope.orig = float(c.rope_original_max_position);
+  dd.rope.beta_fast = c.rope_beta_fast;
+  dd.rope.beta_slow = c.rope_beta_slow;
+  dd.rope.mscale = c.rope_mscale > 0.f ? c.rope_mscale : 1.f;
+  dd.eps = c.rms_eps;
   dd.cache_dt = c.cache_dtype;
   dd.sigma = c.softmax_scale > 0.f ? c.softmax_scale
                                    : 1.0f / std::sqrt(float(dd.dn + dd.dr));
@@ -169,6 +181,7 @@ int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx,
   p->off_slot = L.take(size_t(T) * 8);
   p->off_qs = L.take(size_t(T) * d.H * d.dqk() * act);
   p->off_lat = L.take(size_t(S) * max_ctx * d.W() * act);
+  p->off_kpe = L.take(size_t(S) * max_ctx * d.dr * 2);
   p->off_kv = L.take(size_t(S) * max_ctx * d.H * d.dkv() * act);
   p->bytes = L.top;
   return MLA_OK;

@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "mla.h"
+#include "mla_rope.h"
 
 namespace mla {
 
@@ -17,7 +18,8 @@ struct Dims {
   int W() const { return dc + dr; }      // cached row width
   int dqk() const { return dn + dr; }    // per-head query width
   int dkv() const { return dn + dv; }    // per-head kv_b_proj rows
-  float theta, eps, sigma;
+  RopeParams rope;
+  float eps, sigma;
 };
 
 // Element size in bytes of an mla_dtype (0 for an unknown code).
@@ -99,6 +101,7 @@ struct PrefillPlan {
   size_t off_slot;            // int64 [T]
   size_t off_qs;              // [T][H][dqk] scaled, RoPE'd queries (fp32; fp16 on the bf16 path)
   size_t off_lat;             // act  [S][max_ctx][W] gathered (dequantised) cache rows
+  size_t off_kpe;             // fp16 [S][max_ctx][dr] their k_pe part (bf16 path)
   size_t off_kv;              // [S][max_ctx][H*dkv] decompressed k_nope | v (fp32; fp16 on the bf16 path)
   size_t bytes;
 };

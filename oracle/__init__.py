@@ -19,13 +19,13 @@ brute force.  No page prints a worked numeric example of the attention output, s
 values themselves are pinned only through those checks (see the design notes, "parity
 unpinned").
 """
-from .mla import (Dims, rms_norm, rope, kv_rows, cache_rows, queries, head_weights, softmax,
+from .mla import (Dims, rms_norm, rope, rope_frequencies, kv_rows, cache_rows, queries, head_weights, softmax,
                   attend_explicit, attend_absorbed, decode_one, prefill_chunk)
 from .numerics import (E4M3_MAX, fp32_round, bf16_round, e4m3_quantise, e4m3_encode_values,
                        e4m3_decode_codes, fp8_store, store_rows)
 
 __all__ = [
-    "Dims", "rms_norm", "rope", "kv_rows", "cache_rows", "queries", "head_weights", "softmax",
+    "Dims", "rms_norm", "rope", "rope_frequencies", "kv_rows", "cache_rows", "queries", "head_weights", "softmax",
     "attend_explicit", "attend_absorbed", "decode_one", "prefill_chunk",
     "E4M3_MAX", "fp32_round", "bf16_round", "e4m3_quantise", "e4m3_encode_values",
     "e4m3_decode_codes", "fp8_store", "store_rows",

@@ -42,6 +42,20 @@ class Dims:
     rope_theta: float = 10000.0
     rms_eps: float = 1e-6
     softmax_scale: float = 0.0   # 0: 1/sqrt(d_n + d_r)
+    # YaRN context extension of the rotary embedding (rope_factor <= 1: plain RoPE).  The pages
+    # name YaRN as how the 128K context is reached but give no constants.
+    rope_factor: float = 0.0
+    rope_original_max_position: int = 0
+    rope_beta_fast: float = 0.0
+    rope_beta_slow: float = 0.0
+    rope_mscale: float = 0.0     # 0: 1
+
+    @property
+    def rope_args(self):
+        """Keyword arguments of rope() for this layer."""
+        return dict(factor=self.rope_factor, original=self.rope_original_max_position,
+                    beta_fast=self.rope_beta_fast, beta_slow=self.rope_beta_slow,
+                    mscale=self.rope_mscale or 1.0)
 
     @property
     def sigma(self):
@@ -66,17 +80,37 @@ def rms_norm(v, gamma, eps):
     return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps) * gamma
 
 
-def rope(u, pos, theta):
+def rope_frequencies(d, theta, factor=0.0, original=0, beta_fast=0.0, beta_slow=0.0):
+    """Angular frequency of each pair i < d/2.
+
+    Plain RoPE: f_i = theta**(-2i/d).  With factor s > 1, YaRN's interpolation "by parts"
+    (Peng et al., "YaRN: Efficient Context Window Extension of Large Language Models", the
+    ramp over the number of turns a dimension makes across the original context): a pair whose
+    wavelength 2 pi / f_i fits r = original * f_i / (2 pi) times into the original context keeps
+    its frequency when r >= beta_fast, is slowed by the factor (f_i / s, i.e. plain position
+    interpolation) when r <= beta_slow, and in between takes (1 - g) f_i / s + g f_i with
+    g = (r - beta_slow) / (beta_fast - beta_slow).
+    """
+    f = float(theta) ** (-2.0 * np.arange(d // 2) / d)
+    if factor <= 1.0:
+        return f
+    turns = original * f / (2.0 * np.pi)
+    g = np.clip((turns - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+    return (1.0 - g) * (f / factor) + g * f
+
+
+def rope(u, pos, theta, factor=0.0, original=0, beta_fast=0.0, beta_slow=0.0, mscale=1.0):
     """Rotary embedding of the last axis (even length d) at integer positions pos.
 
-    Pair i = (u[2i], u[2i+1]) is rotated by the angle pos * theta**(-2i/d).  pos broadcasts
-    against u.shape[:-1].  The angle is formed in fp64.
+    Pair i = (u[2i], u[2i+1]) is rotated by the angle pos * f_i (rope_frequencies), and scaled
+    by mscale (1 for the plain rotation).  pos broadcasts against u.shape[:-1].  The angle is
+    formed in fp64.
     """
     u = np.asarray(u, dtype=np.float64)
     d = u.shape[-1]
-    freq = float(theta) ** (-2.0 * np.arange(d // 2) / d)
+    freq = rope_frequencies(d, theta, factor, original, beta_fast, beta_slow)
     ang = np.asarray(pos, dtype=np.float64)[..., None] * freq
-    cos, sin = np.cos(ang), np.sin(ang)
+    cos, sin = mscale * np.cos(ang), mscale * np.sin(ang)
     even, odd = u[..., 0::2], u[..., 1::2]
     out = np.empty(np.broadcast_shapes(u.shape, ang.shape[:-1] + (d,)), dtype=np.float64)
     out[..., 0::2] = even * cos - odd * sin
@@ -95,7 +129,7 @@ def kv_rows(dims, W, x, pos):
     c = a[:, : dims.kv_lora_rank]
     k_pe = a[:, dims.kv_lora_rank:]
     c_hat = rms_norm(c, W["kv_a_norm"], dims.rms_eps)
-    k_hat = rope(k_pe, np.asarray(pos), dims.rope_theta)
+    k_hat = rope(k_pe, np.asarray(pos), dims.rope_theta, **dims.rope_args)
     return np.concatenate([c_hat, k_hat], axis=1)
 
 
@@ -118,7 +152,7 @@ def queries(dims, W, x, pos):
         q = x @ W["q_proj"].T
     q = q.reshape(x.shape[0], dims.heads, dims.qk_nope + dims.qk_rope)
     q_nope = q[..., : dims.qk_nope]
-    q_pe = rope(q[..., dims.qk_nope:], np.asarray(pos)[:, None], dims.rope_theta)
+    q_pe = rope(q[..., dims.qk_nope:], np.asarray(pos)[:, None], dims.rope_theta, **dims.rope_args)
     return q_nope, q_pe
 
 

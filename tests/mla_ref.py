@@ -13,7 +13,8 @@ from mla_latent_kv_compress_amd import inputs
 def oracle_dims(shape):
     return oracle.Dims(shape.hidden_size, shape.num_heads, shape.q_lora_rank, shape.kv_lora_rank,
                        shape.qk_nope_head_dim, shape.qk_rope_head_dim, shape.v_head_dim, shape.rope_theta,
-                       shape.rms_eps, shape.softmax_scale)
+                       shape.rms_eps, shape.softmax_scale, shape.rope_factor, shape.rope_original_max_position,
+                       shape.rope_beta_fast, shape.rope_beta_slow, shape.rope_mscale)
 
 
 def oracle_weights(layer):

@@ -72,6 +72,11 @@ def test_status_strings():
     (dict(act_dtype=7), 1), (dict(cache_dtype=9), 1), (dict(rope_theta=0.0), 1), (dict(rms_eps=-1.0), 1),
     (dict(softmax_scale=float("nan")), 1), (dict(kv_lora_rank=256), 2), (dict(num_heads=24), 2),
     (dict(act_dtype=api.F32, cache_dtype=api.BF16), 2),
+    # YaRN: a factor above 1 needs the original context length and beta_fast > beta_slow >= 0
+    (dict(rope_factor=8.0), 1), (dict(rope_factor=8.0, rope_original_max_position=4096, rope_beta_fast=1.0,
+                                      rope_beta_slow=32.0), 1),
+    (dict(rope_factor=8.0, rope_original_max_position=4096, rope_beta_fast=32.0, rope_beta_slow=-1.0), 1),
+    (dict(rope_mscale=-1.0), 1), (dict(rope_factor=float("inf")), 1),
 ])
 def test_config_validation(bad, code):
     L = api.lib()

@@ -190,6 +190,25 @@ def test_ragged_batch_taken_longest_first(cache):
         assert e <= TOL[cache if cache == "fp8" else "bf16"], (b, e)
 
 
+# YaRN-scaled RoPE (the pages give no constants; these exercise every branch of the ramp: with
+# an original context of 1024 the 32 pairs split into kept, interpolated and mixed ones).
+YARN_DSV2 = dataclasses.replace(DSV2, rope_factor=8.0, rope_original_max_position=1024, rope_beta_fast=32.0,
+                                rope_beta_slow=1.0, rope_mscale=1.1)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_decode_yarn_rope(cache):
+    lengths = [100, 2047, 3000]
+    log(f"decode with YaRN RoPE ({cache} cache)")
+    layer = Layer(YARN_DSV2, "bf16", cache, seed=6)
+    batch = DecodeBatch(layer, wl(YARN_DSV2, "bf16", cache, len(lengths)), seed=6, lengths=lengths)
+    out = batch.run(num_splits=3).float().cpu().numpy()
+    for b in range(len(lengths)):
+        e = rel_err(out[b], decode_reference(layer, batch, b, seed=6))
+        log(f"  seq {b} ctx {lengths[b] + 1}: rel err {e:.2e}")
+        assert e <= TOL[cache if cache == "fp8" else "bf16"], (b, e)
+
+
 def test_bf16_output():
     log("decode bf16 output")
     layer = Layer(DSV2, "bf16", "bf16", seed=1, out_dtype="bf16")

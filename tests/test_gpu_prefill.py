@@ -76,6 +76,28 @@ def test_prefill_matches_oracle(case):
         assert e <= TOL[cache if cache == "fp8" else act], (s, e)
 
 
+def test_prefill_yarn_rope():
+    """Prefill parity with YaRN-scaled RoPE (constants as in the decode test).
+
+    rope_mscale m scales the RoPE part of every score by m^2, and with it the error that the
+    query path's roundings (the bf16 query latent, fp16 queries) leave in the scores, as the
+    peaked decode variant scales its bar with its score scale; the bar is the bf16 one times m^2.
+    (Measured: 1.45e-2 without YaRN, 1.93e-2 with m = 1.1 on the same seed.)
+    """
+    import dataclasses
+    m = 1.1
+    shape = dataclasses.replace(DSV2, rope_factor=8.0, rope_original_max_position=1024, rope_beta_fast=32.0,
+                                rope_beta_slow=1.0, rope_mscale=m)
+    log("prefill with YaRN RoPE")
+    layer = Layer(shape, "bf16", "bf16", seed=7)
+    pf = Prefill(layer, [0, 1500], [300, 200], seed=7)
+    out, cu = pf.run()
+    for s in range(2):
+        e = token_err(out[cu[s]:cu[s + 1]], pf.reference(s))
+        log(f"  seq {s}: rel err {e:.2e}")
+        assert e <= TOL["bf16"] * m * m, (s, e)
+
+
 def test_chunked_equals_whole_and_last_row_equals_decode():
     log("prefill chunking")
     layer = Layer(DSV2, "bf16", "bf16", seed=8)

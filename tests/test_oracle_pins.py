@@ -103,6 +103,55 @@ def test_p6_rope_relative_position():
     np.testing.assert_allclose(dots, dots[0], rtol=1e-10)
 
 
+# YaRN (the pages name YaRN as the route to the 128K context but give no constants; the pins
+# below fix what the method guarantees whatever the constants).
+YARN = dict(factor=40.0, original=4096, beta_fast=32.0, beta_slow=1.0)
+
+
+def test_p6_yarn_off_is_plain_rope():
+    g = np.random.default_rng(4)
+    u = g.standard_normal((3, 64))
+    pos = np.array([5, 4000, 131071])
+    for factor in (0.0, 1.0, 0.5):
+        np.testing.assert_array_equal(oracle.rope(u, pos, 1e4, factor=factor, original=4096, beta_fast=32.0,
+                                                  beta_slow=1.0), oracle.rope(u, pos, 1e4))
+
+
+def test_p6_yarn_by_parts_limits():
+    """Fast pairs (many turns over the original context) keep their rotation; slow pairs (under
+    beta_slow turns) are position-interpolated: at position s * p they turn as plain RoPE at p."""
+    d, s = 64, YARN["factor"]
+    f = 1e4 ** (-2.0 * np.arange(d // 2) / d)
+    turns = YARN["original"] * f / (2 * math.pi)
+    fast, slow = np.where(turns >= 32.0)[0], np.where(turns <= 1.0)[0]
+    assert len(fast) >= 10 and len(slow) >= 4 and 0 in fast and d // 2 - 1 in slow
+    g = np.random.default_rng(5)
+    u = g.standard_normal(d)
+    for p in (1, 777, 50000):
+        y = oracle.rope(u, np.array(p), 1e4, **YARN)
+        plain = oracle.rope(u, np.array(p), 1e4)
+        stretched = oracle.rope(u, np.array(p * s), 1e4, **YARN)
+        for i in fast:
+            np.testing.assert_allclose(y[2 * i:2 * i + 2], plain[2 * i:2 * i + 2], rtol=0, atol=1e-12)
+        for i in slow:
+            np.testing.assert_allclose(stretched[2 * i:2 * i + 2], plain[2 * i:2 * i + 2], rtol=0, atol=1e-9)
+    fy = oracle.rope_frequencies(d, 1e4, **YARN)
+    assert np.all(np.diff(fy) < 0)                      # still strictly slower towards the last pair
+    assert np.all(fy <= f) and np.all(fy >= f / s)      # between position interpolation and none
+
+
+def test_p6_yarn_relative_position_and_mscale():
+    g = np.random.default_rng(6)
+    q, k = g.standard_normal(64), g.standard_normal(64)
+    dots = [oracle.rope(q, np.array(m), 1e4, **YARN) @ oracle.rope(k, np.array(m - 37), 1e4, **YARN)
+            for m in (37, 100, 5000, 131072)]
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-10)
+    m = 1.3
+    scaled = oracle.rope(q, np.array(900), 1e4, mscale=m, **YARN) @ oracle.rope(k, np.array(11), 1e4, mscale=m, **YARN)
+    plain = oracle.rope(q, np.array(900), 1e4, **YARN) @ oracle.rope(k, np.array(11), 1e4, **YARN)
+    np.testing.assert_allclose(scaled, m * m * plain, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- P7: RMSNorm
 def test_p7_rmsnorm_closed_form():
     g = np.random.default_rng(3)
