@@ -474,11 +474,13 @@ __global__ __launch_bounds__(256) void merge_uv_kernel(
 // order are those of merge_uv_kernel.
 constexpr int kMuAhead = 4;
 // NKH: the latent range is cut into NKH parts, one per wave of a row group (2 x NKH waves).
+// The d_v = 128 output columns are cut into 128 / (16 NT) blocks, one per blockIdx.z.
 template <int NT, int OUT, int SPL, int DC, int NKH>
 __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
     int B, int H, int dn, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
-  constexpr int dv = 16 * NT, half = DC / NKH, nk = half / 32;
+  constexpr int dv = 128, half = DC / NKH, nk = half / 32;
+  const int vb = blockIdx.z * 16 * NT;               // this work-group's output columns [vb, vb + 16 NT)
   static_assert(nk >= kMuAhead, "prefetch depth within the K loop");
   __shared__ f32x4_t red[2][NKH - 1][NT][64];       // other parts' sums, [row group][part][tile][lane]
   __shared__ float wts[32][SPL];
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
   const int kbeg = kh * half;
   const float* po = part_o + (long(b < B ? b : 0) * SPL * H + h) * DC + kbeg + kq;
   const long pstride = long(H) * DC;                // between the splits of one (b, h)
-  const uint16_t* wuv = kv_b + (long(h) * (dn + dv) + dn + (lane & 15)) * DC + kbeg + kq;
+  const uint16_t* wuv = kv_b + (long(h) * (dn + dv) + dn + vb + (lane & 15)) * DC + kbeg + kq;
   bf16x8_t wf[kMuAhead][NT];
   float4 xo[kMuAhead][SPL][2];
 #pragma unroll
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int bo = b0 + 16 * rg + 4 * (lane >> 4) + i;
-      if (bo < B) sts_<OUT>(out, (long(bo) * H + h) * dv + 16 * t + (lane & 15), o[i]);
+      if (bo < B) sts_<OUT>(out, (long(bo) * H + h) * dv + vb + 16 * t + (lane & 15), o[i]);
     }
   }
 }
@@ -610,10 +612,18 @@ template <int OUT, int SPL>
 static void launch_merge_uv_fixed(int B, int H, int dn, const float* part_o, const float* part_ml,
                                   const void* kv_b, void* out, hipStream_t st) {
   constexpr int kParts = 4;
-  hipLaunchKernelGGL((merge_uv_fixed_kernel<8, OUT, SPL, 512, kParts>), dim3(H, (B + 31) / 32), dim3(128 * kParts),
-                     0, st, B, H, dn,
-                     part_o, part_ml, static_cast<const uint16_t*>(kv_b),
-                     static_cast<typename StoreT<OUT>::type*>(out));
+  const unsigned rows = unsigned((B + 31) / 32);
+  // Few (head, 32-row) blocks (the Lite shape's 16 heads, a handful of long sequences): cut the
+  // output columns over 2 or 4 work-groups, each streaming that share of W_UV^h.
+  const long blocks = long(H) * rows;
+#define MLA_MUF(NT, Z)                                                                                     \
+  hipLaunchKernelGGL((merge_uv_fixed_kernel<NT, OUT, SPL, 512, kParts>), dim3(H, rows, Z), dim3(128 * kParts), \
+                     0, st, B, H, dn, part_o, part_ml, static_cast<const uint16_t*>(kv_b),                  \
+                     static_cast<typename StoreT<OUT>::type*>(out))
+  if (blocks <= 64) MLA_MUF(2, 4);
+  else if (blocks <= 128) MLA_MUF(4, 2);
+  else MLA_MUF(8, 1);
+#undef MLA_MUF
 }
 
 bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
