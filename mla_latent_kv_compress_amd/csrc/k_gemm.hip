@@ -717,26 +717,40 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
   f32x4_t acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fp32 partials: every K step's values of one split are requested together, so the sum takes
+  // one round trip per split (the splits are added in order).
+  constexpr int kKs = DN / 32;
+  float v[kKs][8];
 #pragma unroll
-  for (int ks = 0; ks < DN / 32; ++ks) {
+  for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[ks][j] = 0.f;
+  if (!QS && b < B) {
+    const float* src = qh + long(b) * nq + 8 * g;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      float4 x[kKs][2];
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        x[ks][0] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks);
+        x[ks][1] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks + 4);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        v[ks][0] += x[ks][0].x; v[ks][1] += x[ks][0].y; v[ks][2] += x[ks][0].z; v[ks][3] += x[ks][0].w;
+        v[ks][4] += x[ks][1].x; v[ks][5] += x[ks][1].y; v[ks][6] += x[ks][1].z; v[ks][7] += x[ks][1].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < kKs; ++ks) {
     typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
     bf16x8v a;
     if constexpr (QS) {
       a = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const bf16x8_t*>(
                                           q_nope16 + (long(min(b, B - 1)) * H + h) * DN + 32 * ks + 8 * g));
     } else {
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (b < B) {
-      const float* src = qh + long(b) * nq + 32 * ks + 8 * g;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float4 x0 = *reinterpret_cast<const float4*>(src + sp * sstride);
-        const float4 x1 = *reinterpret_cast<const float4*>(src + sp * sstride + 4);
-        v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
-        v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
-      }
-    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = (__bf16)(scale * v[j]);
+      for (int j = 0; j < 8; ++j) a[j] = (__bf16)(scale * v[ks][j]);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
