@@ -1,24 +1,24 @@
-// Split-K decode attention over a bf16 latent cache, 64 heads per work-group (weight-absorbed).
+// Split-K decode attention over a bf16 or fp8 latent cache, 64 heads per work-group
+// (weight-absorbed).
 //
 // One work-group of 8 waves per (sequence, split, group of 64 heads), two waves per SIMD with
 // separate roles:
-//   score waves 0-3   wave w owns heads [16w, 16w+16) of the group: S[token][head] = R . Qhat^T
-//                     with v_mfma_f32_16x16x32_bf16 (2 token tiles, 18 K steps over two
-//                     accumulators per tile), the query slice in registers for the whole split;
-//                     online softmax per head in base 2 (log2 e is folded into Qhat); P to LDS.
+//   score waves 0-3   wave w owns token tile w & 1 (16 tokens of each stage) and head half
+//                     w >> 1 (32 heads): S[token][head] = R . Qhat^T with
+//                     v_mfma_f32_16x16x32_bf16 (2 head tiles, 18 K steps over two accumulators
+//                     per tile), the query slice (144 registers) held for the whole split;
+//                     softmax per head in base 2 (log2 e is folded into Qhat); P to LDS.
 //   value waves 4-7   wave 4+w owns latent columns [128w, 128w+128) for the 64 heads:
 //                     O^T[c][head] += R^T . P^T with v_mfma_f32_32x32x16_bf16 (4 column tiles x
-//                     2 head tiles, 2 K steps of 16 tokens), R^T read with ds_read_b64_tr_b16;
+//                     2 head tiles, 2 K steps of 16 tokens), R^T read with transposing LDS reads;
 //                     they also issue the direct global->LDS loads of the cache rows.
-// The split's rows stream through LDS in stages of 32 tokens (32 rows x 576 bf16 = 36 KiB) in a
-// ring of 4, three stages ahead.  Step i runs the value product of stage i next to the score
-// product of stage i + 1 (on different waves of each SIMD, so the matrix core and LDS work of
-// the two overlap), with one work-group barrier per step.  The cached latent is also the value,
-// so one LDS stage feeds both products.  The work-groups of the head groups of one (sequence,
-// split) are dealt to the same XCD next to each other, so they stream the same rows together
-// and the second read of every row is an L2 hit: the cache leaves HBM once per split.  Per SIMD
-// the query slice (72 registers), the fp32 accumulators (128) and the operand prefetch fit the
-// register file of two waves with room to spare.
+// The split's rows stream through LDS in stages of 32 tokens (bf16: 36 KiB, a ring of 4, three
+// stages ahead; fp8: 18 KiB plus the scales, a ring of 8, seven ahead).  Step i runs the value
+// product of stage i next to the score product of stage i + 1 (on different waves of each SIMD),
+// with one work-group barrier per step.  The cached latent is also the value, so one LDS stage
+// feeds both products.  The work-groups of the head groups of one (sequence, split) are dealt to
+// the same XCD next to each other, so they stream the same rows together and the second read of
+// every row is an L2 hit: the cache leaves HBM once per split.
 //
 // LDS: a stage holds rows of 72 16-byte chunks, unpadded (each direct load instruction fills a
 // contiguous KiB), with chunk c of row r stored at c ^ rsw(r), rsw(r) < 8 (the XOR stays inside
@@ -50,6 +50,7 @@
 
 #include "mla_device.h"
 #include "mla_kernels.h"
+#include "mla_lds.h"
 #include "mla_plan.h"
 
 namespace mla {
@@ -125,34 +126,11 @@ __device__ __forceinline__ float sum_across_rows(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Wait until at most `n` vector-memory operations of this wave are outstanding (n a constant).
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF));
-}
-
-// Work-group barrier for LDS traffic only: waits for this wave's LDS operations, not for its
-// outstanding global loads (the ring's prefetches stay in flight across it).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One direct global->LDS load: lane i's 16 bytes at base + off land at LDS byte lds + 16 i.
-// Written as inline assembly so that the compiler does not track it: its own tracking of such
-// loads makes every later LDS read wait for all of them (vmcnt(0)), which would serialise the
-// prefetch ring.  Completion is awaited explicitly (wait_vm) before the barrier that publishes a
-// stage.  The instruction has no register results; its address operands are read at issue.
-__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
-}
+using lds::dma16;
+using lds::dma4;
+using lds::wait_vm;
+__device__ __forceinline__ void lds_barrier() { lds::barrier(); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return lds::addr(p); }
 
 // Offset, within a stage, of the 16 bytes that lane `lane` of direct-load instruction k of wave
 // `wave` fetches: instruction k of wave w fills LDS bytes [(4k + w) KiB, +1 KiB) of the stage;
@@ -167,11 +145,6 @@ __device__ __forceinline__ uint32_t stage_offset(int k, int wave, int lane, int 
   const int c = FP8 ? (cp ^ ((r >> 2) & 3)) : (cp ^ rsw(r));
   const int rs = r < valid ? r : valid - 1;
   return uint32_t(rs * Geo<FP8>::kRowBytes + c * 16);
-}
-
-// Direct load of 4 bytes per lane: lane i's word at base + off lands at LDS byte lds + 4 i.
-__device__ __forceinline__ void dma4(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile("global_load_lds_dword %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 // Wait until at most A * L of this wave's direct loads are outstanding, A the largest of

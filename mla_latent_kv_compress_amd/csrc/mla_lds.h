@@ -1,4 +1,5 @@
-// LDS staging helpers shared by the streaming kernels (prefill attention, large-tile GEMM).
+// LDS staging helpers shared by the streaming kernels (decode and prefill attention, large-tile
+// GEMM).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,6 +30,11 @@ __device__ __forceinline__ void barrier() {
 // barrier that publishes the data.  No register results; the address operands are read at issue.
 __device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// The same with 4 bytes per lane: lane i's word at base + off lands at LDS byte lds + 4 i.
+__device__ __forceinline__ void dma4(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ uint32_t addr(const void* p) {

@@ -175,15 +175,19 @@ def test_decode_loud_token_restart(cache):
         assert e <= TOL["fp8" if cache == "fp8" else "bf16"], e
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8"])
-def test_ragged_batch_taken_longest_first(cache):
+@pytest.mark.parametrize("cache,lengths,splits", [
+    ("bf16", [33, 2000, 64, 1200, 0, 640, 3100, 257], 20),   # 8 x 20 x 2 = 320 work-groups
+    ("fp8", [33, 2000, 64, 1200, 0, 640, 3100, 257], 20),
+    # 20 sequences (not a multiple of the 8 XCDs: plain work-group order), 8 splits: 320 work-groups
+    ("bf16", [int(x) for x in np.random.default_rng(9).integers(0, 700, 20)], 8),
+])
+def test_ragged_batch_taken_longest_first(cache, lengths, splits):
     """Ragged lengths over more work-groups than one round: the sequences are ranked by length on
     the GPU and dispatched longest first; every sequence must still get its own result."""
-    lengths = [33, 2000, 64, 1200, 0, 640, 3100, 257]
-    log(f"decode ragged, ranked ({cache} cache)")
+    log(f"decode ragged, ranked ({cache} cache, B {len(lengths)}, {splits} splits)")
     layer = Layer(DSV2, "bf16", cache, seed=5)
     batch = DecodeBatch(layer, wl(DSV2, "bf16", cache, len(lengths)), seed=5, lengths=lengths)
-    out = batch.run(num_splits=20).float().cpu().numpy()       # 8 x 20 x 2 head groups = 320 work-groups
+    out = batch.run(num_splits=splits).float().cpu().numpy()
     for b in range(len(lengths)):
         e = rel_err(out[b], decode_reference(layer, batch, b, seed=5))
         log(f"  seq {b} ctx {lengths[b] + 1}: rel err {e:.2e}")
