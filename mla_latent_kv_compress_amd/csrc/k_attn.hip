@@ -82,7 +82,8 @@ void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t
     size_t sh = size_t(a.dc + a.dr + 256) * sizeof(float) + 256 * sizeof(long);
     hipLaunchKernelGGL(decode_attn_simt_kernel, dim3(a.H, a.splits, a.B), dim3(256), sh, st, a.H, a.dc,
                        a.dr, a.splits, a.max_blocks, static_cast<const float*>(a.qhat),
-                       static_cast<const float*>(a.cache), a.block_table, a.ctx, a.part_o, a.part_ml);
+                       static_cast<const float*>(a.cache), a.block_table, a.ctx, static_cast<float*>(a.part_o),
+                       a.part_ml);
     return;
   }
   launch_decode_attn_v2(cache, a, st);           // every bf16-path shape (d_c 512, d_r 64, H % 16 == 0)

@@ -38,6 +38,11 @@
 // for the log-sum-exp merge whatever m is.  Rows of a stage beyond the context re-read the last
 // valid row (finite data) and get p = 0.
 //
+// The split's state leaves as (m - k, 2^k l, 2^k O) with O in fp16, k chosen per head so that
+// the largest |O| entry lies in [2^14, 2^15) (the value waves exchange their per-head maxima and
+// the score waves their row sums through LDS): the same state, half the bytes of fp32, and 11
+// significant bits where bf16 would keep 8.
+//
 // fp8 cache (e4m3 codes plus one fp32 scale per token): the same kernel with 576-byte rows, so a
 // 32-token stage is 18 KiB of codes plus the stage's 32 scales, and the ring holds 8 stages.  The
 // codes are converted exactly to bf16 at the operand reads (v_cvt_scalef32_pk_bf16_fp8 with scale
@@ -110,6 +115,24 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  f16x2_t v = {(_Float16)a, (_Float16)b};             // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Exponent k of the power-of-two scale a split's state (m, l, O) leaves with: (m - k, 2^k l,
+// 2^k O) stands for the same 2^m (l, O).  The largest |O| entry a lands in [2^14, 2^15), where
+// fp16 holds it and every entry down to 2^-29 a with 11 significant bits, unless 2^k l would
+// pass 2^100 (a state whose largest entry is below 2^-85 l, i.e. latent values that small).
+__device__ __forceinline__ int part_scale(float a, float l) {
+  if (!(a > 0.f) || a == INFINITY) return 0;        // an empty split (a = 0) keeps its state
+  int ea, el;
+  frexpf(a, &ea);                                    // a < 2^ea
+  frexpf(l, &el);
+  return min(15 - ea, 100 - el);
+}
+
 // Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per 16-lane row) with the gfx950
 // row-swap instructions (VALU, no LDS round trip): permlane16_swap(x, x) returns rows (0,0,2,2)
 // and (1,1,3,3) of x, permlane32_swap(x, x) returns rows (0,1,0,1) and (2,3,2,3).
@@ -177,7 +200,7 @@ template <bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     int H, int splits, int max_blocks, int xcd_map, const uint16_t* __restrict__ qhat,
     const void* __restrict__ cache, const float* __restrict__ cache_scale, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ order, float* __restrict__ part_o,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ order, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml) {
   using Gm = Geo<FP8>;
   constexpr int kRowBytes = Gm::kRowBytes, kSlot = Gm::kSlot, kRing = Gm::kRing, kLoads = Gm::kLoads;
@@ -350,6 +373,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   float* const xm = reinterpret_cast<float*>(pbase + kPBytes);
   float* const lx = reinterpret_cast<float*>(pbase + kPBytes + 2 * kHeads * 4);
   auto hrow = [&](int nt) { return 32 * hh + 16 * nt + li; };
+  // At the end of the split: xa[value wave][head] = largest |O| entry over the wave's columns,
+  // xl[head] = the head's row sum (in the ring, idle by then).
+  float* const xa = reinterpret_cast<float*>(ring);
+  float* const xl = reinterpret_cast<float*>(ring + 4 * kHeads * 4);
   // fp8: scales of the lane's four tokens 16 mt_w + 4 g + j of the current stage (read by scores).
   f32x4_t tsc = f32x4_t{1.f, 1.f, 1.f, 1.f};
 
@@ -579,13 +606,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       totals();
       restart_needed(false, lsum);
     }
+    // Row sums to the value waves, their per-head maxima |O| back (the ring is idle now).
+    if (mt_w == 0 && g == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) xl[hrow(nt)] = lsum[nt];
+    }
+    lds_barrier();
     if (mt_w == 0 && g == 0) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        if (hbase + hrow(nt) >= H) continue;
-        const long row = (long(b) * splits + sp) * H + hbase + hrow(nt);
-        part_ml[row * 2] = m_ref[nt];
-        part_ml[row * 2 + 1] = lsum[nt];
+        const int h = hrow(nt);
+        if (hbase + h >= H) continue;
+        const float a = fmaxf(fmaxf(xa[h], xa[kHeads + h]), fmaxf(xa[2 * kHeads + h], xa[3 * kHeads + h]));
+        const int k = part_scale(a, lsum[nt]);
+        const long row = (long(b) * splits + sp) * H + hbase + h;
+        part_ml[row * 2] = m_ref[nt] - float(k);
+        part_ml[row * 2 + 1] = lsum[nt] * ldexpf(1.f, k);
       }
     }
   } else {
@@ -622,17 +658,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       }
       restart_needed(accumulate(), unused);
     }
-    const long row0 = (long(b) * splits + sp) * H + hbase;
+    // Each head's largest |O| over this wave's 128 columns (the lane and lane ^ 32 hold them).
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      if (hbase + 32 * nt + ph >= H) continue;
-      float* dst = part_o + (row0 + 32 * nt + ph) * kDC + 128 * wave + 4 * (lane >> 5);
+      float a = 0.f;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4_t*>(dst + 32 * ct + 8 * q) =
-              f32x4_t{o[ct][nt][4 * q], o[ct][nt][4 * q + 1], o[ct][nt][4 * q + 2], o[ct][nt][4 * q + 3]};
+        for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(o[ct][nt][e]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+      a = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      if (lane < 32) xa[wave * kHeads + 32 * nt + ph] = a;
+    }
+    lds_barrier();
+    const long row0 = (long(b) * splits + sp) * H + hbase;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int h = 32 * nt + ph;
+      if (hbase + h >= H) continue;
+      const float a = fmaxf(fmaxf(xa[h], xa[kHeads + h]), fmaxf(xa[2 * kHeads + h], xa[3 * kHeads + h]));
+      const float sc = ldexpf(1.f, part_scale(a, xl[h]));
+      uint16_t* dst = part_o + (row0 + h) * kDC + 128 * wave + 4 * (lane >> 5);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)             // 2^k O in fp16 (the merge reads half the bytes)
+          *reinterpret_cast<uint2*>(dst + 32 * ct + 8 * q) =
+              make_uint2(pack_h2(sc * o[ct][nt][4 * q], sc * o[ct][nt][4 * q + 1]),
+                         pack_h2(sc * o[ct][nt][4 * q + 2], sc * o[ct][nt][4 * q + 3]));
     }
   }
 }
@@ -667,7 +720,7 @@ bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t 
   const auto kern = cache_type == K_FP8 ? decode_attn_latent_kernel<true> : decode_attn_latent_kernel<false>;
   hipLaunchKernelGGL(kern, dim3(unsigned(units)), dim3(kThreads), 0, st, a.H, a.splits, a.max_blocks, xcd_map,
                      static_cast<const uint16_t*>(a.qhat), a.cache, a.cache_scale, a.block_table, a.ctx, order,
-                     a.part_o, a.part_ml);
+                     static_cast<uint16_t*>(a.part_o), a.part_ml);
   return true;
 }
 

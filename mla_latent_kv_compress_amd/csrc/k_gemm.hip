@@ -368,116 +368,47 @@ __global__ __launch_bounds__(256) void gemm_skinny_pair_kernel(SkinnyProb p0, Sk
 
 
 // ------------------------------------------------------------------ merge + W_UV (decode)
-// out[b][h][n] = sum_c W_UV^h[n][c] * Otilde[b][h][c] for one head per work-group, where Otilde
+// out[b][h][n] = sum_c W_UV^h[n][c] * Otilde[b][h][c] for the heads' 32-row blocks, where Otilde
 // is the log-sum-exp merge of the attention's split partials, formed on the fly:
 //   m = max_j m_j,  w_j = 2^(m_j - m) / sum_j' 2^(m_j' - m) l_j',  Otilde = sum_j w_j O_j
-// (scores are in base 2).  Otilde is fp32; it enters the bf16 MFMA as a hi + lo pair
-// (hi = bf16(v), lo = bf16(v - hi)), so the product sees it to ~2^-16 relative.  W_UV^h is rows
-// [h (dn + dv) + dn, +dv) of kv_b_proj ([n][c], c contiguous).
-// A work-group serves 32 batch rows of one head with 4 waves: wave w takes rows 16 (w & 1) ..
-// +15 and half of the c range (w >> 1); the two halves' sums meet in LDS.  Each wave merges the
-// partials of its own rows and c range, so every partial is read once.
-template <int NT, int OUT>
-__global__ __launch_bounds__(256) void merge_uv_kernel(
-    int B, int H, int dc, int dn, int splits, const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
-  constexpr int dv = 16 * NT;
-  __shared__ f32x4_t red[2][NT][64];                // second c-half sums, [row group][tile][lane]
-  extern __shared__ float wts[];                    // [32 rows][splits]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = wave & 1, kh = wave >> 1;
-  const int h = blockIdx.x, b0 = blockIdx.y * 32;
-  if (tid < 32) {
-    const int b = b0 + tid;
-    float* w = wts + tid * splits;
-    if (b < B) {
-      const float* ml = part_ml + (long(b) * splits * H + h) * 2;
-      const long step = long(H) * 2;
-      float m = -INFINITY;
-      for (int j = 0; j < splits; ++j) m = fmaxf(m, ml[j * step]);
-      float l = 0.f;
-      for (int j = 0; j < splits; ++j) {
-        const float mj = ml[j * step];
-        const float e = mj == -INFINITY ? 0.f : exp2f(mj - m);
-        w[j] = e;
-        l += e * ml[j * step + 1];
-      }
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      for (int j = 0; j < splits; ++j) w[j] *= inv;
-    } else {
-      for (int j = 0; j < splits; ++j) w[j] = 0.f;
-    }
+// (scores are in base 2).  The partials O_j are fp16 as the attention writes them, or one fp32
+// state when the splits were merged beforehand.  Otilde is summed in fp32 and enters the bf16
+// MFMA as a hi + lo pair (hi = bf16(v), lo = bf16(v - hi)), so the product sees it to ~2^-16
+// relative.  W_UV^h is rows [h (dn + dv) + dn, +dv) of kv_b_proj ([n][c], c contiguous).
+// The split count SPL and the latent width DC are fixed at compile time, so that the K loop
+// unrolls into straight-line code with its loads kMuAhead steps ahead of use (the weights of
+// every split are likewise fetched at once).  Rows past B read row 0 of the partials with merge
+// weight 0 (the partials are finite), so no branch guards the loads.
+// Eight consecutive partials of one split, held as loaded and widened to fp32 at use.
+template <typename P> struct Part8;
+template <> struct Part8<float> {
+  float4 x0, x1;
+  __device__ __forceinline__ void load(const float* p) {
+    x0 = *reinterpret_cast<const float4*>(p);
+    x1 = *reinterpret_cast<const float4*>(p + 4);
   }
-  __syncthreads();
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+  }
+};
+template <> struct Part8<uint16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float* v) const {
+    typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+    const f16x8_t x = __builtin_bit_cast(f16x8_t, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = float(x[i]);
+  }
+};
 
-  const int r = 16 * rg + (lane & 15), b = b0 + r, kq = 8 * (lane >> 4);
-  const int half = dc / 2, kbeg = kh * half;
-  const float* wr = wts + r * splits;
-  const float* po = part_o + (long(b < B ? b : 0) * splits * H + h) * dc + kbeg + kq;
-  const long pstride = long(H) * dc;                // between the splits of one (b, h)
-  const uint16_t* wuv = kv_b + (long(h) * (dn + dv) + dn + (lane & 15)) * dc + kbeg + kq;
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = 0; k < half; k += 32) {
-    bf16x8_t wf[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) wf[t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * dc + k);
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (b < B) {
-#pragma unroll 4
-      for (int j = 0; j < splits; ++j) {
-        const float wj = wr[j];
-        const float4 x0 = *reinterpret_cast<const float4*>(po + j * pstride + k);
-        const float4 x1 = *reinterpret_cast<const float4*>(po + j * pstride + k + 4);
-        v[0] += wj * x0.x; v[1] += wj * x0.y; v[2] += wj * x0.z; v[3] += wj * x0.w;
-        v[4] += wj * x1.x; v[5] += wj * x1.y; v[6] += wj * x1.z; v[7] += wj * x1.w;
-      }
-    }
-    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-    bf16x8v hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hi[e] = (__bf16)v[e];                          // round to nearest even
-      lo[e] = (__bf16)(v[e] - (float)hi[e]);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, wf[t], acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, wf[t], acc[t], 0, 0, 0);
-    }
-  }
-  if (kh == 1) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) red[rg][t][lane] = acc[t];
-  }
-  __syncthreads();
-  if (kh == 1) return;
-  // C layout: lane holds C[4 (lane / 16) + i][lane % 16] of each 16 x 16 tile.
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const f32x4_t o = acc[t] + red[rg][t][lane];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bo = b0 + 16 * rg + 4 * (lane >> 4) + i;
-      if (bo < B) sts_<OUT>(out, (long(bo) * H + h) * dv + 16 * t + (lane & 15), o[i]);
-    }
-  }
-}
-
-// The same merge + projection with the split count SPL and the latent width DC fixed at compile
-// time, so that the K loop unrolls into straight-line code with its loads kMuAhead steps ahead
-// of use (the weights of every split are likewise fetched at once): the generic kernel above
-// waits for each step's loads in turn.  Rows past B read row 0 of the partials with merge
-// weight 0 (the partials are finite), so no branch guards the loads.  The arithmetic and its
-// order are those of merge_uv_kernel.
 constexpr int kMuAhead = 4;
 // NKH: the latent range is cut into NKH parts, one per wave of a row group (2 x NKH waves).
 // The d_v = 128 output columns are cut into 128 / (16 NT) blocks, one per blockIdx.z.
-template <int NT, int OUT, int SPL, int DC, int NKH>
+template <int NT, int OUT, int SPL, int DC, int NKH, typename P>
 __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
-    int B, int H, int dn, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    int B, int H, int dn, const P* __restrict__ part_o, const float* __restrict__ part_ml,
     const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
   constexpr int dv = 128, half = DC / NKH, nk = half / 32;
   const int vb = blockIdx.z * 16 * NT;               // this work-group's output columns [vb, vb + 16 NT)
@@ -504,20 +435,17 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
   __builtin_amdgcn_sched_barrier(0);
   const int r = 16 * rg + (lane & 15), b = b0 + r, kq = 8 * (lane >> 4);
   const int kbeg = kh * half;
-  const float* po = part_o + (long(b < B ? b : 0) * SPL * H + h) * DC + kbeg + kq;
+  const P* po = part_o + (long(b < B ? b : 0) * SPL * H + h) * DC + kbeg + kq;
   const long pstride = long(H) * DC;                // between the splits of one (b, h)
   const uint16_t* wuv = kv_b + (long(h) * (dn + dv) + dn + vb + (lane & 15)) * DC + kbeg + kq;
   bf16x8_t wf[kMuAhead][NT];
-  float4 xo[kMuAhead][SPL][2];
+  Part8<P> xo[kMuAhead][SPL];
 #pragma unroll
   for (int k = 0; k < kMuAhead; ++k) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) wf[k][t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * DC + 32 * k);
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-      xo[k][j][0] = *reinterpret_cast<const float4*>(po + j * pstride + 32 * k);
-      xo[k][j][1] = *reinterpret_cast<const float4*>(po + j * pstride + 32 * k + 4);
-    }
+    for (int j = 0; j < SPL; ++j) xo[k][j].load(po + j * pstride + 32 * k);
   }
   __builtin_amdgcn_sched_barrier(0);
   {
@@ -556,9 +484,10 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
       const float wj = wr[j];
-      const float4 x0 = xo[sl][j][0], x1 = xo[sl][j][1];
-      v[0] += wj * x0.x; v[1] += wj * x0.y; v[2] += wj * x0.z; v[3] += wj * x0.w;
-      v[4] += wj * x1.x; v[5] += wj * x1.y; v[6] += wj * x1.z; v[7] += wj * x1.w;
+      float x[8];
+      xo[sl][j].get(x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += wj * x[e];
     }
     typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
     bf16x8v hi, lo;
@@ -575,10 +504,7 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
 #pragma unroll
       for (int t = 0; t < NT; ++t) wf[sl][t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * DC + kn);
 #pragma unroll
-      for (int j = 0; j < SPL; ++j) {
-        xo[sl][j][0] = *reinterpret_cast<const float4*>(po + j * pstride + kn);
-        xo[sl][j][1] = *reinterpret_cast<const float4*>(po + j * pstride + kn + 4);
-      }
+      for (int j = 0; j < SPL; ++j) xo[sl][j].load(po + j * pstride + kn);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -608,8 +534,8 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
   }
 }
 
-template <int OUT, int SPL>
-static void launch_merge_uv_fixed(int B, int H, int dn, const float* part_o, const float* part_ml,
+template <int OUT, int SPL, typename P>
+static void launch_merge_uv_fixed(int B, int H, int dn, const P* part_o, const float* part_ml,
                                   const void* kv_b, void* out, hipStream_t st) {
   constexpr int kParts = 4;
   const unsigned rows = unsigned((B + 31) / 32);
@@ -617,7 +543,7 @@ static void launch_merge_uv_fixed(int B, int H, int dn, const float* part_o, con
   // output columns over 2 or 4 work-groups, each streaming that share of W_UV^h.
   const long blocks = long(H) * rows;
 #define MLA_MUF(NT, Z)                                                                                     \
-  hipLaunchKernelGGL((merge_uv_fixed_kernel<NT, OUT, SPL, 512, kParts>), dim3(H, rows, Z), dim3(128 * kParts), \
+  hipLaunchKernelGGL((merge_uv_fixed_kernel<NT, OUT, SPL, 512, kParts, P>), dim3(H, rows, Z), dim3(128 * kParts), \
                      0, st, B, H, dn, part_o, part_ml, static_cast<const uint16_t*>(kv_b),                  \
                      static_cast<typename StoreT<OUT>::type*>(out))
   if (blocks <= 64) MLA_MUF(2, 4);
@@ -626,39 +552,28 @@ static void launch_merge_uv_fixed(int B, int H, int dn, const float* part_o, con
 #undef MLA_MUF
 }
 
-bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
+bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const uint16_t* part_o,
                             const float* part_ml, const void* kv_b, void* out, hipStream_t st, float* otilde,
                             float* ml1) {
-  if (dv != 128 || dc % 64 != 0 || splits > 256) return false;
-  if (dc == 512 && splits > 4 && otilde && ml1) {
+  if (dv != 128 || dc != 512 || splits < 1) return false;
+#define MLA_MU(SPL, PO, ML)                                                                             \
+  (out_type == K_BF16 ? launch_merge_uv_fixed<S_BF16, SPL>(B, H, dn, PO, ML, kv_b, out, st)             \
+                      : launch_merge_uv_fixed<S_F32, SPL>(B, H, dn, PO, ML, kv_b, out, st))
+  if (splits > 4) {
+    if (!otilde || !ml1) return false;
     // Many splits: merge them first (every partial read once, one work-group per (b, h)), then
-    // project the single merged state.
+    // project the single merged fp32 state.
     launch_merge_splits(B, H, dc, splits, part_o, part_ml, otilde, ml1, st);
-    splits = 1;
-    part_o = otilde;
-    part_ml = ml1;
-  }
-  if (dc == 512 && splits >= 1 && splits <= 4) {
-#define MLA_MU(SPL)                                                                                     \
-  (out_type == K_BF16 ? launch_merge_uv_fixed<S_BF16, SPL>(B, H, dn, part_o, part_ml, kv_b, out, st)    \
-                      : launch_merge_uv_fixed<S_F32, SPL>(B, H, dn, part_o, part_ml, kv_b, out, st))
-    switch (splits) {
-      case 1: MLA_MU(1); break;
-      case 2: MLA_MU(2); break;
-      case 3: MLA_MU(3); break;
-      default: MLA_MU(4); break;
-    }
-#undef MLA_MU
+    MLA_MU(1, static_cast<const float*>(otilde), static_cast<const float*>(ml1));
     return true;
   }
-  dim3 grid(H, (B + 31) / 32);
-  const size_t sh = size_t(32) * splits * sizeof(float);
-  if (out_type == K_BF16)
-    hipLaunchKernelGGL((merge_uv_kernel<8, S_BF16>), grid, dim3(256), sh, st, B, H, dc, dn, splits, part_o, part_ml,
-                       static_cast<const uint16_t*>(kv_b), static_cast<uint16_t*>(out));
-  else
-    hipLaunchKernelGGL((merge_uv_kernel<8, S_F32>), grid, dim3(256), sh, st, B, H, dc, dn, splits, part_o, part_ml,
-                       static_cast<const uint16_t*>(kv_b), static_cast<float*>(out));
+  switch (splits) {
+    case 1: MLA_MU(1, part_o, part_ml); break;
+    case 2: MLA_MU(2, part_o, part_ml); break;
+    case 3: MLA_MU(3, part_o, part_ml); break;
+    default: MLA_MU(4, part_o, part_ml); break;
+  }
+#undef MLA_MU
   return true;
 }
 

@@ -379,9 +379,10 @@ void launch_prefill_prep(int S, int max_q, const int32_t* cu, const int32_t* sta
 // For each (b, h): m = max_j m_j, w_j = 2^(m_j - m), otilde = sum_j w_j o_j / sum_j w_j l_j.
 // Partial states use base-2 exponents (scores carry a log2 e factor).  Empty splits have
 // m_j = -inf and l_j = 0 and weigh nothing.
+// (HILO, the bf16 path: fp16 partials, otilde written as a bf16 hi + lo pair; else fp32 throughout.)
 template <bool HILO>
 __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int splits,
-                                                           const float* __restrict__ part_o,
+                                                           const void* __restrict__ part_o_,
                                                            const float* __restrict__ part_ml,
                                                            void* __restrict__ otilde) {
   extern __shared__ float wts[];                    // [splits] normalised split weights
@@ -400,18 +401,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int sp
   l = block_sum(l, red);                            // also orders the wts writes before the reads
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   const long stride = long(H) * dc;                 // between consecutive splits of one (b, h)
-  const float* po = part_o + (long(b) * splits * H + h) * dc;
+  const long base = (long(b) * splits * H + h) * dc;
+  auto po = [&](long i) {
+    return HILO ? float(static_cast<const _Float16*>(part_o_)[base + i]) : static_cast<const float*>(part_o_)[base + i];
+  };
   for (int c = threadIdx.x; c < dc; c += blockDim.x) {
     float v = 0.f;
     int s = 0;
     for (; s + 4 <= splits; s += 4) {
       float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = po[(s + j) * stride + c];
+      for (int j = 0; j < 4; ++j) x[j] = po((s + j) * stride + c);
 #pragma unroll
       for (int j = 0; j < 4; ++j) v += wts[s + j] * x[j];
     }
-    for (; s < splits; ++s) v += wts[s] * po[s * stride + c];
+    for (; s < splits; ++s) v += wts[s] * po(s * stride + c);
     v *= inv;
     if (HILO) {
       uint16_t* o = static_cast<uint16_t*>(otilde) + (long(b) * H + h) * 2 * dc;
@@ -428,7 +432,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int sp
 // (dc % 4 == 0) and ml1[b][h] = (0, 1), the state of one already-normalised split.  A work-group
 // of 128 threads per (b, h) reads four columns per thread and eight splits per step, so the
 // partials of every split are in flight together.
-__global__ __launch_bounds__(128) void merge_splits_kernel(int H, int dc, int splits, const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void merge_splits_kernel(int H, int dc, int splits, const uint16_t* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            float* __restrict__ otilde, float* __restrict__ ml1) {
   extern __shared__ float wts[];                    // [splits] normalised split weights
@@ -447,14 +451,19 @@ __global__ __launch_bounds__(128) void merge_splits_kernel(int H, int dc, int sp
   l = block_sum(l, red);                            // also orders the wts writes before the reads
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   const long stride = long(H) * dc;                 // between consecutive splits of one (b, h)
-  const float* po = part_o + (long(b) * splits * H + h) * dc;
+  const uint16_t* po = part_o + (long(b) * splits * H + h) * dc;
+  auto load4 = [&](long i) {                        // four fp16 partials as floats
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    const f16x4_t u = *reinterpret_cast<const f16x4_t*>(po + i);
+    return make_float4(float(u[0]), float(u[1]), float(u[2]), float(u[3]));
+  };
   for (int c = 4 * threadIdx.x; c < dc; c += 4 * blockDim.x) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     int s = 0;
     for (; s + 8 <= splits; s += 8) {
       float4 x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const float4*>(po + (s + j) * stride + c);
+      for (int j = 0; j < 8; ++j) x[j] = load4((s + j) * stride + c);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float w = wts[s + j];
@@ -462,7 +471,7 @@ __global__ __launch_bounds__(128) void merge_splits_kernel(int H, int dc, int sp
       }
     }
     for (; s < splits; ++s) {
-      const float4 x = *reinterpret_cast<const float4*>(po + s * stride + c);
+      const float4 x = load4(s * stride + c);
       const float w = wts[s];
       v.x += w * x.x; v.y += w * x.y; v.z += w * x.z; v.w += w * x.w;
     }
@@ -475,13 +484,13 @@ __global__ __launch_bounds__(128) void merge_splits_kernel(int H, int dc, int sp
   }
 }
 
-void launch_merge_splits(int B, int H, int dc, int splits, const float* part_o, const float* part_ml, float* otilde,
-                         float* ml1, hipStream_t st) {
+void launch_merge_splits(int B, int H, int dc, int splits, const uint16_t* part_o, const float* part_ml,
+                         float* otilde, float* ml1, hipStream_t st) {
   hipLaunchKernelGGL(merge_splits_kernel, dim3(H, B), dim3(128), size_t(splits) * 4, st, H, dc, splits, part_o,
                      part_ml, otilde, ml1);
 }
 
-void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
+void launch_decode_merge(int act, int B, int H, int dc, int splits, const void* part_o,
                          const float* part_ml, void* otilde, hipStream_t st) {
   if (act == K_F32)
     hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(H, B), dim3(256), size_t(splits) * 4, st, H, dc, splits,

@@ -248,7 +248,7 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   a.qhat = qhat;
   a.cache = cache->data; a.cache_scale = cache->scale;
   a.block_table = block_table; a.max_blocks = max_blocks; a.ctx = context_lens;
-  a.part_o = reinterpret_cast<float*>(at(workspace, p.off_part_o));
+  a.part_o = at(workspace, p.off_part_o);
   a.part_ml = reinterpret_cast<float*>(at(workspace, p.off_part_ml));
   a.order = p.ordered ? reinterpret_cast<int32_t*>(at(workspace, p.off_order)) : nullptr;
   if (ev_attn_begin) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_begin), s);
@@ -259,7 +259,8 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   // out[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  The bf16 path
   // merges the split partials inside the projection kernel.
   if (path == PATH_BF16 && launch_decode_merge_uv(kdt(cfg->out_dtype), B, d.H, d.dc, d.dn, d.dv, p.splits,
-                                                  a.part_o, a.part_ml, w->kv_b_proj, out, s,
+                                                  static_cast<const uint16_t*>(a.part_o), a.part_ml,
+                                                  w->kv_b_proj, out, s,
                                                   reinterpret_cast<float*>(otilde),
                                                   reinterpret_cast<float*>(at(workspace, p.off_ml1))))
     return finish();

@@ -87,7 +87,8 @@ struct DecodeAttnArgs {
   const void* cache; const float* cache_scale;
   const int32_t* block_table; int max_blocks;
   const int32_t* ctx;
-  float* part_o; float* part_ml;
+  void* part_o;              // [B][splits][H][dc]: fp32 on the fp32 path, fp16 (scaled state) on the bf16 path
+  float* part_ml;
   int32_t* order = nullptr;   // [B] scratch: sequences by length, longest first (64-head kernel)
 };
 void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st);
@@ -102,12 +103,14 @@ bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t 
 // out[b][h] = W_UV^h Otilde[b][h], out fp32 or bf16 per out_type; false if the shape does not apply.
 // With more than 4 splits (dc 512) and the two fp32 scratch buffers otilde [B][H][dc] and
 // ml1 [B][H][2], the splits are merged by a first kernel and the projection reads the result.
-bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const float* part_o,
+// The bf16 path's partials O_j are fp16 (the attention scales each (split, head) state by a power of two).
+bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, int splits, const uint16_t* part_o,
                             const float* part_ml, const void* kv_b, void* out, hipStream_t st,
                             float* otilde = nullptr, float* ml1 = nullptr);
-void launch_merge_splits(int B, int H, int dc, int splits, const float* part_o, const float* part_ml, float* otilde,
-                         float* ml1, hipStream_t st);
-void launch_decode_merge(int act, int B, int H, int dc, int splits, const float* part_o,
+void launch_merge_splits(int B, int H, int dc, int splits, const uint16_t* part_o, const float* part_ml,
+                         float* otilde, float* ml1, hipStream_t st);
+// part_o: fp32 (act K_F32) or fp16 (act K_BF16) partials.
+void launch_decode_merge(int act, int B, int H, int dc, int splits, const void* part_o,
                          const float* part_ml, void* otilde, hipStream_t st);
 
 // Prefill: gather (and dequantise) each sequence's cached rows [0, ctx) into lat [S][max_ctx][W];

@@ -159,7 +159,7 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   p->off_qnope = L.take(size_t(B) * d.H * d.dn * act);
   p->off_rope = L.take(size_t(B) * d.dr * 4);
   p->off_qhat = L.take(size_t(B) * d.H * d.W() * act);
-  p->off_part_o = L.take(size_t(B) * p->splits * d.H * d.dc * 4);
+  p->off_part_o = L.take(size_t(B) * p->splits * d.H * d.dc * (path == PATH_F32 ? 4 : 2));
   p->off_part_ml = L.take(size_t(B) * p->splits * d.H * 2 * 4);
   const int hpg = decode_heads_per_group(d, path);
   // (with many splits per sequence every work-group is short and their order matters little)
