@@ -44,7 +44,9 @@
  *                                           multiples of 8
  * Precision of the bf16 path: weights, hidden states and the cache are read as stored;
  * products accumulate in fp32.  Decode scores the cache with the absorbed query rounded to
- * bf16 and weights the latents with bf16 probabilities; prefill rounds queries, decompressed
+ * bf16 and weights the latents with bf16 probabilities; each split's softmax state is handed to
+ * the merge in fp16 under a per-head power-of-two scale (11 significant bits of every entry
+ * within 2^-29 of the head's largest); prefill rounds queries, decompressed
  * keys / values and probabilities to fp16 (all are of moderate range) before its MFMAs.
  */
 #ifndef MLA_H
