@@ -15,7 +15,7 @@ namespace mla {
 // read.  The next K step is prefetched into registers while the current one computes.
 template <int BM, int BN, int BK, bool NN, int OUT>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
-    int M, int N, int K, int kchunk, int kwrap, const uint16_t* __restrict__ X, long lda, long sx,
+    int M, int N, int K, int kchunk, const uint16_t* __restrict__ X, long lda, long sx,
     const uint16_t* __restrict__ W, long ldw, long sw, typename StoreT<OUT>::type* __restrict__ Y,
     long ldc, long sy, long ssplit, float alpha, int nsplit) {
   constexpr int LDK = BK + 8;                       // padded row: 16-lane reads hit distinct banks
@@ -50,8 +50,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
       if (!NN) {
         int row = c / (BK / 8), kq = (c % (BK / 8)) * 8;
         int gn = n0 + row, gk = k + kq;
-        int wk = kwrap ? gk % kwrap : gk;
-        rb[i] = (gn < N && gk < k1) ? *reinterpret_cast<const uint4*>(W + gn * ldw + wk) : make_uint4(0, 0, 0, 0);
+        rb[i] = (gn < N && gk < k1) ? *reinterpret_cast<const uint4*>(W + gn * ldw + gk) : make_uint4(0, 0, 0, 0);
       } else {
         int krow = c / (BN / 8), nq = (c % (BN / 8)) * 8;
         int gk = k + krow, gn = n0 + nq;
@@ -710,7 +709,7 @@ template <int BM, int BN, int BK, bool NN, int OUT>
 static void launch_bf16(const GemmArgs& g, hipStream_t st) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.batch * g.nsplit);
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, NN, OUT>), grid, dim3(256), 0, st, g.M, g.N, g.K,
-                     g.kchunk, g.kwrap, static_cast<const uint16_t*>(g.X), g.lda, g.sx,
+                     g.kchunk, static_cast<const uint16_t*>(g.X), g.lda, g.sx,
                      static_cast<const uint16_t*>(g.W), g.ldw, g.sw,
                      static_cast<typename StoreT<OUT>::type*>(g.Y), g.ldc, g.sy, g.ssplit, g.alpha, g.nsplit);
 }
@@ -718,7 +717,7 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
 // The skinny kernel's conditions: TN, M <= 64, K and the chunk in 64-steps, 16-byte rows, and
 // per-operand offsets that fit the 32-bit load offsets.
 static bool skinny_ok(const GemmArgs& g) {
-  return g.kind == GEMM_BF16 && !g.nn && g.M <= 64 && g.kwrap == 0 && g.K % 64 == 0 && g.kchunk % 64 == 0 &&
+  return g.kind == GEMM_BF16 && !g.nn && g.M <= 64 && g.K % 64 == 0 && g.kchunk % 64 == 0 &&
          g.lda % 8 == 0 && g.ldw % 8 == 0 && long(g.M) * g.lda * 2 < (1L << 32) &&
          long(g.N) * g.ldw * 2 < (1L << 32);
 }

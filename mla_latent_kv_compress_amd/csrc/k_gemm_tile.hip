@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
 }
 
 bool launch_gemm_tile(const GemmArgs& g, hipStream_t st) {
-  if (g.kind != GEMM_BF16 || g.nn || g.kwrap != 0 || g.nsplit != 1) return false;
+  if (g.kind != GEMM_BF16 || g.nn || g.nsplit != 1) return false;
   if (g.out != K_BF16 && g.out != K_F16) return false;
   if (g.K % kTK != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || g.ldw % 8 != 0 || g.ldc % 8 != 0) return false;
   if (g.sx % 8 != 0 || g.sw % 8 != 0 || g.sy % 8 != 0) return false;

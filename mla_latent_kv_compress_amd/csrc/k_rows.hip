@@ -379,12 +379,11 @@ void launch_prefill_prep(int S, int max_q, const int32_t* cu, const int32_t* sta
 // For each (b, h): m = max_j m_j, w_j = 2^(m_j - m), otilde = sum_j w_j o_j / sum_j w_j l_j.
 // Partial states use base-2 exponents (scores carry a log2 e factor).  Empty splits have
 // m_j = -inf and l_j = 0 and weigh nothing.
-// (HILO, the bf16 path: fp16 partials, otilde written as a bf16 hi + lo pair; else fp32 throughout.)
-template <bool HILO>
+// (The fp32 path's merge, fp32 throughout.)
 __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int splits,
-                                                           const void* __restrict__ part_o_,
+                                                           const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
-                                                           void* __restrict__ otilde) {
+                                                           float* __restrict__ otilde) {
   extern __shared__ float wts[];                    // [splits] normalised split weights
   __shared__ float red[16];
   const int h = blockIdx.x, b = blockIdx.y;
@@ -401,30 +400,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(int H, int dc, int sp
   l = block_sum(l, red);                            // also orders the wts writes before the reads
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   const long stride = long(H) * dc;                 // between consecutive splits of one (b, h)
-  const long base = (long(b) * splits * H + h) * dc;
-  auto po = [&](long i) {
-    return HILO ? float(static_cast<const _Float16*>(part_o_)[base + i]) : static_cast<const float*>(part_o_)[base + i];
-  };
+  const float* po = part_o + (long(b) * splits * H + h) * dc;
   for (int c = threadIdx.x; c < dc; c += blockDim.x) {
     float v = 0.f;
     int s = 0;
     for (; s + 4 <= splits; s += 4) {
       float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = po((s + j) * stride + c);
+      for (int j = 0; j < 4; ++j) x[j] = po[(s + j) * stride + c];
 #pragma unroll
       for (int j = 0; j < 4; ++j) v += wts[s + j] * x[j];
     }
-    for (; s < splits; ++s) v += wts[s] * po(s * stride + c);
-    v *= inv;
-    if (HILO) {
-      uint16_t* o = static_cast<uint16_t*>(otilde) + (long(b) * H + h) * 2 * dc;
-      const uint16_t hi = f2bf(v);
-      o[c] = hi;
-      o[dc + c] = f2bf(v - bf2f(hi));
-    } else {
-      static_cast<float*>(otilde)[(long(b) * H + h) * dc + c] = v;
-    }
+    for (; s < splits; ++s) v += wts[s] * po[s * stride + c];
+    otilde[(long(b) * H + h) * dc + c] = v * inv;
   }
 }
 
@@ -490,14 +478,10 @@ void launch_merge_splits(int B, int H, int dc, int splits, const uint16_t* part_
                      part_ml, otilde, ml1);
 }
 
-void launch_decode_merge(int act, int B, int H, int dc, int splits, const void* part_o,
-                         const float* part_ml, void* otilde, hipStream_t st) {
-  if (act == K_F32)
-    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(H, B), dim3(256), size_t(splits) * 4, st, H, dc, splits,
-                       part_o, part_ml, otilde);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(H, B), dim3(256), size_t(splits) * 4, st, H, dc, splits,
-                       part_o, part_ml, otilde);
+void launch_decode_merge(int B, int H, int dc, int splits, const float* part_o, const float* part_ml,
+                         float* otilde, hipStream_t st) {
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(H, B), dim3(256), size_t(splits) * 4, st, H, dc, splits, part_o,
+                     part_ml, otilde);
 }
 
 // ------------------------------------------------------------------ prefill gather

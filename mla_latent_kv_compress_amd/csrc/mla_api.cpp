@@ -21,12 +21,11 @@ int finish() { return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 // output storage (K_F32 / K_BF16 / K_F16; the fp32 path always writes fp32).
 GemmArgs gemm(Path path, bool nn, int out, int M, int N, int K, SplitK sk, int batch, const void* X,
               long lda, long sx, const void* W, long ldw, long sw, void* Y, long ldc, long sy,
-              float alpha = 1.f, int kwrap = 0) {
+              float alpha = 1.f) {
   GemmArgs g;
   g.kind = path == PATH_F32 ? GEMM_F32 : GEMM_BF16;
   g.nn = nn;
   g.out = path == PATH_F32 ? K_F32 : out;
-  g.kwrap = kwrap;
   g.M = M; g.N = N; g.K = K;
   g.kchunk = sk.chunk; g.nsplit = sk.n; g.batch = batch;
   g.X = X; g.lda = lda; g.sx = sx;
@@ -255,22 +254,21 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   launch_decode_attn(act, kdt(cfg->cache_dtype), a, s);
   if (ev_attn_end) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_end), s);
 
-  void* otilde = at(workspace, p.off_otilde);
+  float* otilde = reinterpret_cast<float*>(at(workspace, p.off_otilde));
   // out[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  The bf16 path
-  // merges the split partials inside the projection kernel.
-  if (path == PATH_BF16 && launch_decode_merge_uv(kdt(cfg->out_dtype), B, d.H, d.dc, d.dn, d.dv, p.splits,
-                                                  static_cast<const uint16_t*>(a.part_o), a.part_ml,
-                                                  w->kv_b_proj, out, s,
-                                                  reinterpret_cast<float*>(otilde),
-                                                  reinterpret_cast<float*>(at(workspace, p.off_ml1))))
+  // merges the split partials inside the projection kernel (its shape checks admit only the
+  // d_c 512, d_v 128 it requires).
+  if (path == PATH_BF16) {
+    if (!launch_decode_merge_uv(kdt(cfg->out_dtype), B, d.H, d.dc, d.dn, d.dv, p.splits,
+                                static_cast<const uint16_t*>(a.part_o), a.part_ml, w->kv_b_proj, out, s, otilde,
+                                reinterpret_cast<float*>(at(workspace, p.off_ml1))))
+      return MLA_ERR_UNSUPPORTED;
     return finish();
-  launch_decode_merge(act, B, d.H, d.dc, p.splits, a.part_o, a.part_ml, otilde, s);
-  // On the bf16 path otilde is [hi | lo] (2 dc wide) and both halves meet the same weight row.
+  }
+  launch_decode_merge(B, d.H, d.dc, p.splits, static_cast<const float*>(a.part_o), a.part_ml, otilde, s);
   const char* w_uv = static_cast<const char*>(w->kv_b_proj) + size_t(d.dn) * d.dc * asz;
-  const int kx = path == PATH_F32 ? d.dc : 2 * d.dc;
-  launch_gemm(gemm(path, false, kdt(cfg->out_dtype), B, d.dv, kx, whole(kx), d.H, otilde, long(d.H) * kx, kx,
-                   w_uv, d.dc, long(d.dkv()) * d.dc, out, long(d.H) * d.dv, d.dv, 1.f,
-                   path == PATH_F32 ? 0 : d.dc), s);
+  launch_gemm(gemm(path, false, kdt(cfg->out_dtype), B, d.dv, d.dc, whole(d.dc), d.H, otilde, long(d.H) * d.dc, d.dc,
+                   w_uv, d.dc, long(d.dkv()) * d.dc, out, long(d.H) * d.dv, d.dv), s);
   return finish();
 }
 

@@ -14,8 +14,6 @@ struct GemmArgs {
   int kind;                  // GEMM_F32 (fp32 in/out) or GEMM_BF16 (bf16 in, fp32 accumulate)
   bool nn;                   // W is [K][N] (else [N][K])
   int out;                   // bf16 path output: K_F32, K_BF16 or K_F16
-  int kwrap;                 // TN only: W column index is k % kwrap (0: k), so X = [x_hi | x_lo]
-                             // of width 2 * kwrap reuses one weight row for both halves
   int M, N, K;
   int kchunk, nsplit;        // K split into nsplit slices of kchunk (multiple of 32)
   int batch;
@@ -97,9 +95,7 @@ void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t
 // the work-groups take them longest first.
 bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t st);
 
-// Log-sum-exp merge of split partials, normalised.  fp32 path: otilde [B][H][dc] fp32; bf16
-// path: otilde [B][H][2*dc] = [hi | lo] with hi = bf16(v), lo = bf16(v - hi).
-// Merge of the split partials fused with the W_UV projection (bf16 path, dv = 128):
+// Merge of the split partials fused with the W_UV projection (bf16 path, dc = 512, dv = 128):
 // out[b][h] = W_UV^h Otilde[b][h], out fp32 or bf16 per out_type; false if the shape does not apply.
 // With more than 4 splits (dc 512) and the two fp32 scratch buffers otilde [B][H][dc] and
 // ml1 [B][H][2], the splits are merged by a first kernel and the projection reads the result.
@@ -109,9 +105,9 @@ bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, 
                             float* otilde = nullptr, float* ml1 = nullptr);
 void launch_merge_splits(int B, int H, int dc, int splits, const uint16_t* part_o, const float* part_ml,
                          float* otilde, float* ml1, hipStream_t st);
-// part_o: fp32 (act K_F32) or fp16 (act K_BF16) partials.
-void launch_decode_merge(int act, int B, int H, int dc, int splits, const void* part_o,
-                         const float* part_ml, void* otilde, hipStream_t st);
+// The fp32 path's merge: otilde [B][H][dc] fp32.
+void launch_decode_merge(int B, int H, int dc, int splits, const float* part_o, const float* part_ml,
+                         float* otilde, hipStream_t st);
 
 // Prefill: gather (and dequantise) each sequence's cached rows [0, ctx) into lat [S][max_ctx][W];
 // with kpe16 also their k_pe part (columns [dc, W)) in fp16 into kpe16 [S][max_ctx][W - dc].

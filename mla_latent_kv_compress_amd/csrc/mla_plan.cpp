@@ -165,7 +165,7 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   // (with many splits per sequence every work-group is short and their order matters little)
   p->ordered = hpg == 64 && B <= kOrderMax && p->splits <= 8 && long(B) * p->splits * cdiv(d.H, hpg) > kDecodeRound;
   p->off_order = L.take(size_t(B) * 4);
-  p->off_otilde = L.take(size_t(B) * d.H * d.dc * (path == PATH_F32 ? 4 : 2 * 2));
+  p->off_otilde = L.take(size_t(B) * d.H * d.dc * 4);
   p->off_ml1 = L.take(size_t(B) * d.H * 2 * 4);
   p->bytes = L.top;
   return MLA_OK;

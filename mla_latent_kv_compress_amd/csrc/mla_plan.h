@@ -87,7 +87,7 @@ struct DecodePlan {
   size_t off_qhat;            // act  [B][H][W]    absorbed, scaled query
   size_t off_part_o;          // [B][splits][H][dc]: fp32 on the fp32 path, else fp16
   size_t off_part_ml;         // fp32 [B][splits][H][2]
-  size_t off_otilde;          // f32 [B][H][dc], or bf16 [B][H][2*dc] = [hi | lo] halves (same bytes)
+  size_t off_otilde;          // fp32 [B][H][dc]: the merged state (many splits on the bf16 path)
   size_t off_ml1;             // fp32 [B][H][2]: merged state (0, 1) when the splits are merged first
   size_t bytes;
 };
