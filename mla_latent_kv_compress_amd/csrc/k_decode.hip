@@ -227,8 +227,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       const int k = unit >> 3;
       const int k2 = k / G;
       hg = k - k2 * G;
-      b = (k2 / splits) * 8 + (unit & 7);
-      sp = k2 - (k2 / splits) * splits;
+      if (xcd_map == 1) {                                  // 8 sequences, one split, per round
+        b = (k2 / splits) * 8 + (unit & 7);
+        sp = k2 - (k2 / splits) * splits;
+      } else {                                             // 8 (sequence, split) units per round
+        const int u = k2 * 8 + (unit & 7);
+        b = u / splits;
+        sp = u - b * splits;
+      }
     } else {
       hg = unit % G;
       const int k2 = unit / G;
@@ -711,7 +717,9 @@ bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t 
   if (a.H % 16 != 0 || a.dc != kDC || a.dr != kDR) return false;
   if (cache_type != K_BF16 && cache_type != K_FP8) return false;
   const long units = long(a.B) * a.splits * ((a.H + kHeads - 1) / kHeads);
-  const int xcd_map = (a.B % 8 == 0) ? 1 : 0;
+  // (the head groups of one (sequence, split) share an XCD: by sequences when B % 8 == 0, else by
+  // (sequence, split) units when B * splits % 8 == 0)
+  const int xcd_map = (a.B % 8 == 0) ? 1 : (long(a.B) * a.splits % 8 == 0) ? 2 : 0;
   const int32_t* order = nullptr;
   if (a.order && a.B <= kOrderMax) {
     hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, st, a.B, a.ctx, a.order);

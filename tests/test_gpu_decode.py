@@ -206,8 +206,12 @@ def test_decode_loud_token_within_slack(cache):
 @pytest.mark.parametrize("cache,lengths,splits", [
     ("bf16", [33, 2000, 64, 1200, 0, 640, 3100, 257], 20),   # 8 x 20 x 2 = 320 work-groups
     ("fp8", [33, 2000, 64, 1200, 0, 640, 3100, 257], 20),
-    # 20 sequences (not a multiple of the 8 XCDs: plain work-group order), 8 splits: 320 work-groups
+    # 20 sequences (not a multiple of the 8 XCDs), 8 splits: 320 work-groups, the head groups of
+    # each (sequence, split) paired on one XCD
     ("bf16", [int(x) for x in np.random.default_rng(9).integers(0, 700, 20)], 8),
+    # 21 sequences x 7 splits = 147 (sequence, split) units, not a multiple of 8: plain work-group
+    # order over the XCDs, still ranked (294 work-groups)
+    ("bf16", [int(x) for x in np.random.default_rng(10).integers(0, 700, 21)], 7),
 ])
 def test_ragged_batch_taken_longest_first(cache, lengths, splits):
     """Ragged lengths over more work-groups than one round: the sequences are ranked by length on
