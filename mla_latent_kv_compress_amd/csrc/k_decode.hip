@@ -198,7 +198,7 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 template <bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
-    int H, int splits, int max_blocks, int xcd_map, const uint16_t* __restrict__ qhat,
+    int H, int splits, int max_blocks, int by_seq, int nunits, const uint16_t* __restrict__ qhat,
     const void* __restrict__ cache, const float* __restrict__ cache_scale, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ order, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml) {
@@ -216,30 +216,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   const int wave = wid & 3;                                // index within the role
   const int g = lane >> 4, li = lane & 15;
   // Work-group -> (sequence slot, split, head group).  Work-groups are dealt to the 8 XCDs
-  // round-robin; with xcd_map the head groups of one (sequence, split) land on the same XCD in
-  // consecutive rounds.  Slots go to sequences in `order` (longest first) when it is given, so
+  // round-robin; the head groups of one (sequence, split) land on the same XCD in consecutive
+  // rounds (by_seq: eight sequences' splits per round, B % 8 == 0; else eight (sequence, split)
+  // units per round, their count nunits padded to a multiple of 8 by work-groups that leave at
+  // once).  Slots go to sequences in `order` (longest first) when it is given, so
   // the long sequences' work-groups are dispatched first and the short ones fill in behind them.
   const int G = (H + kHeads - 1) / kHeads;                  // the last group may be partial
   int b, sp, hg;
   {
     const int unit = blockIdx.x;
-    if (xcd_map) {
-      const int k = unit >> 3;
-      const int k2 = k / G;
-      hg = k - k2 * G;
-      if (xcd_map == 1) {                                  // 8 sequences, one split, per round
-        b = (k2 / splits) * 8 + (unit & 7);
-        sp = k2 - (k2 / splits) * splits;
-      } else {                                             // 8 (sequence, split) units per round
-        const int u = k2 * 8 + (unit & 7);
-        b = u / splits;
-        sp = u - b * splits;
-      }
+    const int k = unit >> 3;
+    const int k2 = k / G;
+    hg = k - k2 * G;
+    if (by_seq) {
+      b = (k2 / splits) * 8 + (unit & 7);
+      sp = k2 - (k2 / splits) * splits;
     } else {
-      hg = unit % G;
-      const int k2 = unit / G;
-      b = k2 / splits;
-      sp = k2 - b * splits;
+      const int u = k2 * 8 + (unit & 7);
+      if (u >= nunits) return;                             // padding (uniform over the work-group)
+      b = u / splits;
+      sp = u - b * splits;
     }
     if (order) b = order[b];
   }
@@ -716,18 +712,18 @@ __global__ __launch_bounds__(1024) void seq_order_kernel(int B, const int32_t* _
 bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t st) {
   if (a.H % 16 != 0 || a.dc != kDC || a.dr != kDR) return false;
   if (cache_type != K_BF16 && cache_type != K_FP8) return false;
-  const long units = long(a.B) * a.splits * ((a.H + kHeads - 1) / kHeads);
-  // (the head groups of one (sequence, split) share an XCD: by sequences when B % 8 == 0, else by
-  // (sequence, split) units when B * splits % 8 == 0)
-  const int xcd_map = (a.B % 8 == 0) ? 1 : (long(a.B) * a.splits % 8 == 0) ? 2 : 0;
+  const int by_seq = a.B % 8 == 0 ? 1 : 0;
+  const long nunits = long(a.B) * a.splits;
+  const long G = (a.H + kHeads - 1) / kHeads;
+  const long grid = by_seq ? nunits * G : (nunits + 7) / 8 * 8 * G;
   const int32_t* order = nullptr;
   if (a.order && a.B <= kOrderMax) {
     hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, st, a.B, a.ctx, a.order);
     order = a.order;
   }
   const auto kern = cache_type == K_FP8 ? decode_attn_latent_kernel<true> : decode_attn_latent_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(unsigned(units)), dim3(kThreads), 0, st, a.H, a.splits, a.max_blocks, xcd_map,
-                     static_cast<const uint16_t*>(a.qhat), a.cache, a.cache_scale, a.block_table, a.ctx, order,
+  hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), 0, st, a.H, a.splits, a.max_blocks, by_seq,
+                     int(nunits), static_cast<const uint16_t*>(a.qhat), a.cache, a.cache_scale, a.block_table, a.ctx, order,
                      static_cast<uint16_t*>(a.part_o), a.part_ml);
   return true;
 }

@@ -209,8 +209,8 @@ def test_decode_loud_token_within_slack(cache):
     # 20 sequences (not a multiple of the 8 XCDs), 8 splits: 320 work-groups, the head groups of
     # each (sequence, split) paired on one XCD
     ("bf16", [int(x) for x in np.random.default_rng(9).integers(0, 700, 20)], 8),
-    # 21 sequences x 7 splits = 147 (sequence, split) units, not a multiple of 8: plain work-group
-    # order over the XCDs, still ranked (294 work-groups)
+    # 21 sequences x 7 splits = 147 (sequence, split) units, padded to 152 by work-groups that
+    # leave at once; ranked (294 working work-groups)
     ("bf16", [int(x) for x in np.random.default_rng(10).integers(0, 700, 21)], 7),
 ])
 def test_ragged_batch_taken_longest_first(cache, lengths, splits):
