@@ -18,7 +18,8 @@
 // LDS rows are swizzled per 16-byte chunk: k_nope chunk c of key r at c ^ (r & 15) (256-byte
 // rows), k_pe at c ^ ((r >> 1) & 7) (128-byte rows), v at c ^ (2 (r & 7)); the direct loads place
 // every chunk where the operand reads expect it (a load instruction fills one contiguous KiB).
-// Query tiles are dispatched heaviest (latest in the chunk, most keys) first.
+// The query tiles of one (head, sequence) run back to back on one XCD, heaviest (latest in the
+// chunk, most keys) first, so their key and value reads are shared through that XCD's L2.
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_lds.h"
@@ -89,9 +90,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Work-groups are dealt to the 8 XCDs round-robin: (head, sequence) pair P runs on XCD P % 8,
+  // its nqt query tiles one after another there (heaviest first), so they stream the same keys
+  // and values at about the same time and all but the first read of each tile hit that XCD's L2.
+  // The pair count is padded to a multiple of 8 by work-groups that leave at once.
   const int L = blockIdx.x;
-  const int qt = nqt - 1 - L / (H * S);            // heaviest query tiles first
-  const int h = (L % (H * S)) % H, s = (L % (H * S)) / H;
+  const int t = L >> 3, g = t / nqt, j = t - g * nqt;
+  const int P = 8 * g + (L & 7);
+  if (P >= H * S) return;
+  const int qt = nqt - 1 - j;
+  const int h = P % H, s = P / H;
   const int q_begin = cu[s], len = cu[s + 1] - q_begin, st0 = start[s];
   if (qt * kQT >= len) return;                     // the whole work-group leaves together
   const int ctx = st0 + len;
@@ -258,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
 bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st) {
   if (a.dn != 128 || a.dr != 64 || a.dv != 128 || a.dc != 512) return false;
   const int nqt = (a.max_q + kQT - 1) / kQT;
-  const dim3 grid(unsigned(long(nqt) * a.H * a.S));
+  const dim3 grid(unsigned(8L * nqt * ((long(a.H) * a.S + 7) / 8)));
   if (a.out_type == K_BF16)
     hipLaunchKernelGGL(prefill_attn_fa_kernel<S_BF16>, grid, dim3(256), 0, st, a.H, a.S, nqt, a.max_ctx, a.cu,
                        a.start, static_cast<const uint16_t*>(a.qs), static_cast<const uint16_t*>(a.kv),
