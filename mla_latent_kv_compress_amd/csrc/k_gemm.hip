@@ -173,17 +173,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     }
 }
 
-// ------------------------------------------------------------------ skinny bf16 GEMM (M <= 64)
-// Y = alpha X W^T for M <= 64 rows (a decode batch): the weight stream is the whole cost, so
+// ------------------------------------------------------------------ skinny bf16 GEMM (M <= 128)
+// Y = alpha X W^T for M <= 128 rows (a decode batch): the weight stream is the whole cost, so
 // each work-group owns 64 or 96 output columns and streams its [columns x K-chunk] slice of W
 // (and the matching slice of X, an L2 hit) through a ring of LDS stages with direct
-// global->LDS loads, several stages ahead of the MFMAs.  A stage is 64 k of X (64 rows) and of W,
+// global->LDS loads, several stages ahead of the MFMAs.  A stage is 64 k of X (MR = 64 or 128
+// rows) and of W,
 // rows of 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), so the 16 rows
 // of an MFMA operand read fall on distinct banks.  Rows past M (or N) re-read the last valid
 // row; their outputs are not stored.  Requires K and the K chunk to be multiples of 64.
 namespace {
-template <int BN> constexpr int sk_stage_bytes() { return (64 + BN) * 128; }
-// Ring depth: 4 stages (16 or 20 KiB each), three stages of loads in flight.  (Measured: a
+template <int BN, int MR> constexpr int sk_stage_bytes() { return (MR + BN) * 128; }
+// Ring depth: 4 stages (16 to 28 KiB each), three stages of loads in flight.  (Measured: a
 // 7-stage ring for the one-per-CU 96-column tiles made the 236B-shaped q_b and kv_a + q_a
 // projections slower, not faster.)
 template <int BN> constexpr int sk_stages() { return 4; }
@@ -225,17 +226,20 @@ struct SkinnyProb {
 // the absorb kernel rotates.  This is the rounding that kernel applies to the fp32 projection.
 constexpr int kOutQSplit = 7;
 
-// Output tile (64 rows x BN columns from column tile nx) of batch-and-split index z.  BN is 64 or
-// 96: a stage holds the X tile (64 rows x 64 k) and the W tile (BN rows x 64 k), rows of 128
-// bytes, (64 + BN) / 8 direct-load instructions of 1 KiB (8 rows each) dealt round-robin to the
-// four waves; wave (wm, wn) computes rows 32 wm .. +32 and columns BN / 2 wn .. + BN / 2.
-template <int OUT, int BN>
+// Output tile (MR rows x BN columns from column tile nx) of batch-and-split index z.  BN is 64 or
+// 96, MR 64 or 128: a stage holds the X tile (MR rows x 64 k) and the W tile (BN rows x 64 k),
+// rows of 128 bytes, (MR + BN) / 8 direct-load instructions of 1 KiB (8 rows each) dealt
+// round-robin to the four waves; wave (wm, wn) computes rows MR / 2 wm .. + MR / 2 and columns
+// BN / 2 wn .. + BN / 2.
+template <int OUT, int BN, int MR>
 __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, char* ring) {
-  constexpr int kStageB = sk_stage_bytes<BN>();
+  constexpr int kStageB = sk_stage_bytes<BN, MR>();
   constexpr int S = sk_stages<BN>();
-  constexpr int NQ = (64 + BN) / 8 / 4;                  // load instructions per wave per stage
+  constexpr int NQ = (MR + BN) / 8 / 4;                  // load instructions per wave per stage
   constexpr int NC = BN / 32;                            // 16-column tiles per wave
-  static_assert((64 + BN) % 32 == 0, "whole instructions per wave");
+  constexpr int MT = MR / 32;                            // 16-row tiles per wave
+  constexpr int XK = MR / 8;                             // KiBs of the stage that hold X
+  static_assert((MR + BN) % 32 == 0, "whole instructions per wave");
   const int M = p.M, N = p.N, K = p.K, kchunk = p.kchunk, nsplit = p.nsplit;
   const long lda = p.lda, ldw = p.ldw, ldc = p.ldc;
   const float alpha = p.alpha;
@@ -250,14 +254,14 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
   const int nk = (min(K, k0 + kchunk) - k0) / 64;      // 64-wide K steps of this split
   const int n0 = nx * BN;
 
-  // Instruction q = wave + 4 j fills KiB q of the stage: q < 8 are X rows 8q .. +7, the rest W
-  // rows 8 (q - 8) .. +7 (lane i -> row + (i >> 3), stored chunk i & 7).
+  // Instruction q = wave + 4 j fills KiB q of the stage: q < XK are X rows 8q .. +7, the rest W
+  // rows 8 (q - XK) .. +7 (lane i -> row + (i >> 3), stored chunk i & 7).
   uint32_t off[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int q = wave + 4 * j;
-    const bool isx = q < 8;
-    const int r = 8 * (isx ? q : q - 8) + (lane >> 3);
+    const bool isx = q < XK;
+    const int r = 8 * (isx ? q : q - XK) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     off[j] = isx ? uint32_t((long(min(r, M - 1)) * lda + 8 * c) * 2) : uint32_t((long(min(n0 + r, N - 1)) * ldw + 8 * c) * 2);
   }
@@ -267,8 +271,8 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     const long kb = long(k0 + 64 * jj) * 2;
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const int q = wave + 4 * j;                       // uniform: q < 8 selects X
-      sk_dma16(reinterpret_cast<const char*>(q < 8 ? X : W) + kb, off[j], sk_lds_addr(st + q * 1024));
+      const int q = wave + 4 * j;                       // uniform: q < XK selects X
+      sk_dma16(reinterpret_cast<const char*>(q < XK ? X : W) + kb, off[j], sk_lds_addr(st + q * 1024));
     }
   };
   auto wait_for = [&](int jj) {                         // stage jj landed (this wave's part)
@@ -284,15 +288,15 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     }
   };
 
-  f32x4_t acc[2][NC];
+  f32x4_t acc[MT][NC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NC; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // operand rows and their chunk XOR
-  int arow[2], brow[NC];
+  int arow[MT], brow[NC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) arow[i] = 32 * wm + 16 * i + (lane & 15);
+  for (int i = 0; i < MT; ++i) arow[i] = (MR / 2) * wm + 16 * i + (lane & 15);
 #pragma unroll
   for (int i = 0; i < NC; ++i) brow[i] = (BN / 2) * wn + 16 * i + (lane & 15);
   const int g = lane >> 4;
@@ -306,29 +310,29 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     const char* st = ring + (i % S) * kStageB;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t af[2], bf[NC];
+      bf16x8_t af[MT], bf[NC];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < MT; ++t)
         af[t] = *reinterpret_cast<const bf16x8_t*>(st + arow[t] * 128 + 16 * ((4 * kk + g) ^ ((arow[t] >> 1) & 7)));
 #pragma unroll
       for (int t = 0; t < NC; ++t)
-        bf[t] = *reinterpret_cast<const bf16x8_t*>(st + 8192 + brow[t] * 128 +
+        bf[t] = *reinterpret_cast<const bf16x8_t*>(st + MR * 128 + brow[t] * 128 +
                                                    16 * ((4 * kk + g) ^ ((brow[t] >> 1) & 7)));
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < MT; ++a)
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
     }
   }
   // C layout: lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile.
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int gn = n0 + (BN / 2) * wn + 16 * c + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int gm = 32 * wm + 16 * a + 4 * (lane >> 4) + r;
+        const int gm = (MR / 2) * wm + 16 * a + 4 * (lane >> 4) + r;
         if (gm < M && gn < N) {
           if constexpr (OUT == kOutQSplit) {
             const int hh = gn / 192, cc = gn - 192 * hh, HH = N / 192;
@@ -344,24 +348,24 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     }
 }
 
-template <int OUT, int BN>
+template <int OUT, int BN, int MR>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyProb p) {
-  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN>()];
-  skinny_tile<OUT, BN>(p, blockIdx.x, blockIdx.z, ring);
+  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN, MR>()];
+  skinny_tile<OUT, BN, MR>(p, blockIdx.x, blockIdx.z, ring);
 }
 
 // Two independent skinny problems in one launch: work-groups [0, tiles0) take p0's tiles,
 // the rest p1's (one launch instead of two dependent-free ones back to back).
-template <int OUT, int BN>
+template <int OUT, int BN, int MR>
 __global__ __launch_bounds__(256) void gemm_skinny_pair_kernel(SkinnyProb p0, SkinnyProb p1, int tiles0) {
-  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN>()];
+  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN, MR>()];
   const int id = blockIdx.x;
   if (id < tiles0) {
     const int nx = (p0.N + BN - 1) / BN;
-    skinny_tile<OUT, BN>(p0, id % nx, id / nx, ring);
+    skinny_tile<OUT, BN, MR>(p0, id % nx, id / nx, ring);
   } else {
     const int nx = (p1.N + BN - 1) / BN;
-    skinny_tile<OUT, BN>(p1, (id - tiles0) % nx, (id - tiles0) / nx, ring);
+    skinny_tile<OUT, BN, MR>(p1, (id - tiles0) % nx, (id - tiles0) / nx, ring);
   }
 }
 
@@ -714,10 +718,10 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
                      static_cast<typename StoreT<OUT>::type*>(g.Y), g.ldc, g.sy, g.ssplit, g.alpha, g.nsplit);
 }
 
-// The skinny kernel's conditions: TN, M <= 64, K and the chunk in 64-steps, 16-byte rows, and
+// The skinny kernel's conditions: TN, M <= 128, K and the chunk in 64-steps, 16-byte rows, and
 // per-operand offsets that fit the 32-bit load offsets.
 static bool skinny_ok(const GemmArgs& g) {
-  return g.kind == GEMM_BF16 && !g.nn && g.M <= 64 && g.K % 64 == 0 && g.kchunk % 64 == 0 &&
+  return g.kind == GEMM_BF16 && !g.nn && g.M <= 128 && g.K % 64 == 0 && g.kchunk % 64 == 0 &&
          g.lda % 8 == 0 && g.ldw % 8 == 0 && long(g.M) * g.lda * 2 < (1L << 32) &&
          long(g.N) * g.ldw * 2 < (1L << 32);
 }
@@ -740,13 +744,16 @@ static void launch_bf16_shape(const GemmArgs& g, hipStream_t st) {
     // 96-column tiles when they fill the CUs in whole rounds and 64-column tiles do not (fewer,
     // better balanced work-groups, each re-reading X for more columns)
     const long z = long(g.batch) * g.nsplit;
+#define MLA_SK(BN, MR, NX) \
+  hipLaunchKernelGGL((gemm_skinny_kernel<OUT, BN, MR>), dim3(NX, 1, unsigned(z)), dim3(256), 0, st, skinny_prob(g))
     if (g.N % 96 == 0 && (g.N / 96) * z % 256 == 0 && ((g.N + 63) / 64) * z % 256 != 0) {
-      hipLaunchKernelGGL((gemm_skinny_kernel<OUT, 96>), dim3(g.N / 96, 1, unsigned(z)), dim3(256), 0, st,
-                         skinny_prob(g));
+      if (g.M <= 64) MLA_SK(96, 64, g.N / 96);
+      else MLA_SK(96, 128, g.N / 96);
       return;
     }
-    hipLaunchKernelGGL((gemm_skinny_kernel<OUT, 64>), dim3((g.N + 63) / 64, 1, unsigned(z)), dim3(256), 0, st,
-                       skinny_prob(g));
+    if (g.M <= 64) MLA_SK(64, 64, (g.N + 63) / 64);
+    else MLA_SK(64, 128, (g.N + 63) / 64);
+#undef MLA_SK
     return;
   }
   if (g.M <= 64)
@@ -768,10 +775,14 @@ bool launch_q_split_gemm(const GemmArgs& g, float* q_pe, hipStream_t st) {
   if (!skinny_ok(g) || g.nsplit != 1 || g.batch != 1 || g.N % 192 != 0) return false;
   SkinnyProb p = skinny_prob(g);
   p.Y2 = q_pe;
-  if (g.N % 96 == 0 && (g.N / 96) % 256 == 0)
-    hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 96>), dim3(g.N / 96, 1, 1), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 64>), dim3(g.N / 64, 1, 1), dim3(256), 0, st, p);
+  const bool w96 = g.N % 96 == 0 && (g.N / 96) % 256 == 0;
+  if (g.M <= 64) {
+    if (w96) hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 96, 64>), dim3(g.N / 96, 1, 1), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 64, 64>), dim3(g.N / 64, 1, 1), dim3(256), 0, st, p);
+  } else {
+    if (w96) hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 96, 128>), dim3(g.N / 96, 1, 1), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 64, 128>), dim3(g.N / 64, 1, 1), dim3(256), 0, st, p);
+  }
   return true;
 }
 
@@ -783,12 +794,18 @@ bool launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t st) {
   const long t0 = long((a.N + bn - 1) / bn) * a.batch * a.nsplit;
   const long t1 = long((b.N + bn - 1) / bn) * b.batch * b.nsplit;
   if (t0 + t1 > (1L << 31) - 1) return false;
-  if (bn == 96)
-    hipLaunchKernelGGL((gemm_skinny_pair_kernel<S_F32, 96>), dim3(unsigned(t0 + t1)), dim3(256), 0, st,
-                       skinny_prob(a), skinny_prob(b), int(t0));
-  else
-    hipLaunchKernelGGL((gemm_skinny_pair_kernel<S_F32, 64>), dim3(unsigned(t0 + t1)), dim3(256), 0, st,
-                       skinny_prob(a), skinny_prob(b), int(t0));
+#define MLA_SKP(BN, MR)                                                                                  \
+  hipLaunchKernelGGL((gemm_skinny_pair_kernel<S_F32, BN, MR>), dim3(unsigned(t0 + t1)), dim3(256), 0, st, \
+                     skinny_prob(a), skinny_prob(b), int(t0))
+  const bool m64 = a.M <= 64 && b.M <= 64;
+  if (bn == 96) {
+    if (m64) MLA_SKP(96, 64);
+    else MLA_SKP(96, 128);
+  } else {
+    if (m64) MLA_SKP(64, 64);
+    else MLA_SKP(64, 128);
+  }
+#undef MLA_SKP
   return true;
 }
 

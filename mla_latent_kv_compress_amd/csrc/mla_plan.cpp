@@ -92,7 +92,7 @@ SplitK gemm_splitk(long M, long N, long K, int tile_m, int tile_n) {
 }
 
 SplitK pair_splitk(long M, long N0, long N1, long K) {
-  if (M > 64 || N0 % 96 != 0 || N1 % 96 != 0 || K % 64 != 0 || K <= 0) return SplitK{0, 0};
+  if (M > 128 || N0 % 96 != 0 || N1 % 96 != 0 || K % 64 != 0 || K <= 0) return SplitK{0, 0};
   const long tiles = N0 / 96 + N1 / 96;
   long n = 256 / tiles;
   if (n < 1) n = 1;
