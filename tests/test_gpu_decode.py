@@ -105,17 +105,19 @@ def test_decode_matches_oracle(case, splits):
         assert e <= TOL[cache if cache == "fp8" else act], (b, e)
 
 
-def test_decode_batch_above_64_rows():
+@pytest.mark.parametrize("B", [100, 140])
+def test_decode_large_batches(B):
     """100 sequences: the decode projections run as 128-row weight-streaming tiles (rows 64..127
-    in the second half of each tile, rows 100..127 past the batch), compared with the oracle on
-    sequences from both halves and the last one."""
-    lengths = [int(x) for x in np.random.default_rng(12).integers(0, 160, 100)]
-    log("decode 100 sequences (128-row projection tiles)")
+    in the second half of each tile, rows 100..127 past the batch).  140 sequences: beyond those
+    tiles, the general front (tiled GEMMs, separate norm and row kernels, query packing).
+    Compared with the oracle on sequences from every 64-row block and the last one."""
+    lengths = [int(x) for x in np.random.default_rng(12).integers(0, 160, B)]
+    log(f"decode {B} sequences")
     layer = Layer(DSV2, "bf16", "bf16", seed=12)
     batch = DecodeBatch(layer, wl(DSV2, "bf16", "bf16", len(lengths)), seed=12, lengths=lengths)
     out = batch.run(num_splits=2).float().cpu().numpy()
     assert np.isfinite(out).all()
-    for b in (0, 31, 63, 64, 77, 99):
+    for b in sorted({0, 31, 63, 64, 77, B - 1} | ({128, 133} if B > 128 else set())):
         e = rel_err(out[b], decode_reference(layer, batch, b, seed=12))
         log(f"  seq {b} ctx {lengths[b] + 1}: rel err {e:.2e}")
         assert e <= TOL["bf16"], (b, e)
