@@ -173,10 +173,10 @@ def _loud_history(cache, factor, seed=4):
 
 
 def _loud_compare(cache, layer, batch, rows, s2, loud, splits_list):
-    """Compare the heads where the loud token's weight is neither ~1 nor ~0 (its score within 16
-    log2 units of the others' log-sum-exp) are left out: there the bf16 rounding of the
-    absorbed query, scaled by the token's huge score, moves its weight by more than the bar, an
-    effect of the score scale alone.  Every output must be finite."""
+    """Compare with the oracle, leaving out the heads where the loud token's weight is neither ~1
+    nor ~0 (its score within 16 log2 units of the others' log-sum-exp): there the bf16 rounding
+    of the absorbed query, scaled by the token's huge score, moves its weight by more than the
+    bar, an effect of the score scale alone.  Every output must be finite."""
     others = np.delete(s2, loud, axis=1)
     mx = others.max(axis=1)
     lse = np.log2(np.sum(np.exp2(others - mx[:, None]), axis=1)) + mx
