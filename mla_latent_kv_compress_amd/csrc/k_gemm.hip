@@ -379,9 +379,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_pair_kernel(SkinnyProb p0, Sk
 // MFMA as a hi + lo pair (hi = bf16(v), lo = bf16(v - hi)), so the product sees it to ~2^-16
 // relative.  W_UV^h is rows [h (dn + dv) + dn, +dv) of kv_b_proj ([n][c], c contiguous).
 // The split count SPL and the latent width DC are fixed at compile time, so that the K loop
-// unrolls into straight-line code with its loads kMuAhead steps ahead of use (the weights of
+// unrolls into straight-line code with its loads AH steps ahead of use (the weights of
 // every split are likewise fetched at once).  Rows past B read row 0 of the partials with merge
 // weight 0 (the partials are finite), so no branch guards the loads.
+
 // Eight consecutive partials of one split, held as loaded and widened to fp32 at use.
 template <typename P> struct Part8;
 template <> struct Part8<float> {
@@ -406,24 +407,27 @@ template <> struct Part8<uint16_t> {
   }
 };
 
-constexpr int kMuAhead = 4;
-// NKH: the latent range is cut into NKH parts, one per wave of a row group (2 x NKH waves).
+// NKH: the latent range is cut into NKH parts.  RT = 1: two waves per part, one per 16-row tile
+// (2 x NKH waves); RT = 2: one wave per part covering both row tiles (NKH waves), so W_UV is
+// requested once per work-group rather than once per row tile (the request stream, not the
+// bytes, bounds this kernel when every CU holds one work-group).  AH: K steps prefetched.
 // The d_v = 128 output columns are cut into 128 / (16 NT) blocks, one per blockIdx.z.
-template <int NT, int OUT, int SPL, int DC, int NKH, typename P>
-__global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
+template <int NT, int OUT, int SPL, int DC, int NKH, typename P, int RT, int AH>
+__global__ __launch_bounds__(64 * NKH * (2 / RT)) void merge_uv_fixed_kernel(
     int B, int H, int dn, const P* __restrict__ part_o, const float* __restrict__ part_ml,
     const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
   constexpr int dv = 128, half = DC / NKH, nk = half / 32;
   const int vb = blockIdx.z * 16 * NT;               // this work-group's output columns [vb, vb + 16 NT)
-  static_assert(nk >= kMuAhead, "prefetch depth within the K loop");
-  __shared__ f32x4_t red[2][NKH - 1][NT][64];       // other parts' sums, [row group][part][tile][lane]
+  static_assert(nk >= AH, "prefetch depth within the K loop");
+  __shared__ f32x4_t red[2][NKH - 1][NT][64];       // other parts' sums, [row tile][part][tile][lane]
   __shared__ float wts[32][SPL];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = wave & 1, kh = wave >> 1;          // row group, latent part
+  const int rg = RT == 1 ? (wave & 1) : 0;          // first row tile of this wave
+  const int kh = RT == 1 ? (wave >> 1) : wave;      // latent part
   const int h = blockIdx.x, b0 = blockIdx.y * 32;
   // Order of the requests: the merge statistics (every thread fetches its row's, tid & 31, so no
-  // branch splits the loads), then the first kMuAhead steps of partials and weights, and only
-  // then the wait for the statistics: the main stream is already in flight across the barrier.
+  // branch splits the loads), then the first AH steps of partials and weights, and only then the
+  // wait for the statistics: the main stream is already in flight across the barrier.
   float mj[SPL], lj[SPL];
   {
     const int bm = min(b0 + (tid & 31), B - 1);       // (tid & 31: every thread, rows alike)
@@ -436,23 +440,30 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int r = 16 * rg + (lane & 15), b = b0 + r, kq = 8 * (lane >> 4);
+  const int kq = 8 * (lane >> 4);
   const int kbeg = kh * half;
-  const P* po = part_o + (long(b < B ? b : 0) * SPL * H + h) * DC + kbeg + kq;
-  const long pstride = long(H) * DC;                // between the splits of one (b, h)
+  const P* po[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int b = b0 + 16 * (rg + t) + (lane & 15);
+    po[t] = part_o + (long(b < B ? b : 0) * SPL * H + h) * DC + kbeg + kq;
+  }
+  const long pstride = long(H) * DC;
   const uint16_t* wuv = kv_b + (long(h) * (dn + dv) + dn + vb + (lane & 15)) * DC + kbeg + kq;
-  bf16x8_t wf[kMuAhead][NT];
-  Part8<P> xo[kMuAhead][SPL];
+  bf16x8_t wf[AH][NT];
+  Part8<P> xo[AH][RT][SPL];
 #pragma unroll
-  for (int k = 0; k < kMuAhead; ++k) {
+  for (int k = 0; k < AH; ++k) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) wf[k][t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * DC + 32 * k);
+    for (int c = 0; c < NT; ++c) wf[k][c] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * c) * DC + 32 * k);
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) xo[k][j].load(po + j * pstride + 32 * k);
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) xo[k][t][j].load(po[t] + j * pstride + 32 * k);
   }
   __builtin_amdgcn_sched_barrier(0);
   {
-    // (every thread computes its row's weights and stores them, the 8 copies of a row alike: a
+    // (every thread computes its row's weights and stores them, the copies of a row alike: a
     // store guarded by tid < 32 would let the compiler sink the statistics loads behind the
     // stream)
     const int b = b0 + (tid & 31);
@@ -471,70 +482,85 @@ __global__ __launch_bounds__(128 * NKH) void merge_uv_fixed_kernel(
   }
   __syncthreads();
 
-  float wr[SPL];
+  float wr[RT][SPL];
 #pragma unroll
-  for (int j = 0; j < SPL; ++j) wr[j] = wts[r][j];
-  f32x4_t acc[NT];
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < SPL; ++j) wr[t][j] = wts[16 * (rg + t) + (lane & 15)][j];
+  f32x4_t acc[RT][NT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[t][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // (scheduling barriers keep the source order: the compiler would otherwise move each load
   // next to its use and shorten the prefetch distance to nothing)
 #pragma unroll
   for (int k = 0; k < nk; ++k) {
     __builtin_amdgcn_sched_barrier(0);
-    const int sl = k % kMuAhead;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-      const float wj = wr[j];
-      float x[8];
-      xo[sl][j].get(x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += wj * x[e];
-    }
+    const int sl = k % AH;
     typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-    bf16x8v hi, lo;
+    bf16x8v hi[RT], lo[RT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      hi[e] = (__bf16)v[e];                          // round to nearest even
-      lo[e] = (__bf16)(v[e] - (float)hi[e]);
+    for (int t = 0; t < RT; ++t) {
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const float wj = wr[t][j];
+        float x[8];
+        xo[sl][t][j].get(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += wj * x[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[t][e] = (__bf16)v[e];                     // round to nearest even
+        lo[t][e] = (__bf16)(v[e] - (float)hi[t][e]);
+      }
     }
     bf16x8_t w[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[t] = wf[sl][t];
-    if (k + kMuAhead < nk) {                         // refill the slot kMuAhead steps ahead
-      const int kn = 32 * (k + kMuAhead);
+    for (int c = 0; c < NT; ++c) w[c] = wf[sl][c];
+    if (k + AH < nk) {                               // refill the slot AH steps ahead
+      const int kn = 32 * (k + AH);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) wf[sl][t] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * t) * DC + kn);
+      for (int c = 0; c < NT; ++c) wf[sl][c] = *reinterpret_cast<const bf16x8_t*>(wuv + long(16 * c) * DC + kn);
 #pragma unroll
-      for (int j = 0; j < SPL; ++j) xo[sl][j].load(po + j * pstride + kn);
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) xo[sl][t][j].load(po[t] + j * pstride + kn);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, w[t], acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, w[t], acc[t], 0, 0, 0);
-    }
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[t], w[c], acc[t][c], 0, 0, 0);
+        acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[t], w[c], acc[t][c], 0, 0, 0);
+      }
   }
   if (kh > 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[rg][kh - 1][t][lane] = acc[t];
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < NT; ++c) red[rg + t][kh - 1][c][lane] = acc[t][c];
   }
   __syncthreads();
   if (kh > 0) return;
   // C layout: lane holds C[4 (lane / 16) + i][lane % 16] of each 16 x 16 tile.  The parts are
   // added in order.
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    f32x4_t o = acc[t];
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int q = 0; q < NKH - 1; ++q) o += red[rg][q][t][lane];
+    for (int c = 0; c < NT; ++c) {
+      f32x4_t o = acc[t][c];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bo = b0 + 16 * rg + 4 * (lane >> 4) + i;
-      if (bo < B) sts_<OUT>(out, (long(bo) * H + h) * dv + vb + 16 * t + (lane & 15), o[i]);
+      for (int q = 0; q < NKH - 1; ++q) o += red[rg + t][q][c][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bo = b0 + 16 * (rg + t) + 4 * (lane >> 4) + i;
+        if (bo < B) sts_<OUT>(out, (long(bo) * H + h) * dv + vb + 16 * c + (lane & 15), o[i]);
+      }
     }
-  }
 }
 
 template <int OUT, int SPL, typename P>
@@ -543,15 +569,16 @@ static void launch_merge_uv_fixed(int B, int H, int dn, const P* part_o, const f
   constexpr int kParts = 4;
   const unsigned rows = unsigned((B + 31) / 32);
   // Few (head, 32-row) blocks (the Lite shape's 16 heads, a handful of long sequences): cut the
-  // output columns over 2 or 4 work-groups, each streaming that share of W_UV^h.
+  // output columns over 2 or 4 work-groups of 8 waves, each streaming that share of W_UV^h.
+  // Many: one work-group of 4 waves per block.
   const long blocks = long(H) * rows;
-#define MLA_MUF(NT, Z)                                                                                     \
-  hipLaunchKernelGGL((merge_uv_fixed_kernel<NT, OUT, SPL, 512, kParts, P>), dim3(H, rows, Z), dim3(128 * kParts), \
-                     0, st, B, H, dn, part_o, part_ml, static_cast<const uint16_t*>(kv_b),                  \
-                     static_cast<typename StoreT<OUT>::type*>(out))
-  if (blocks <= 64) MLA_MUF(2, 4);
-  else if (blocks <= 128) MLA_MUF(4, 2);
-  else MLA_MUF(8, 1);
+#define MLA_MUF(NT, Z, RT, AH)                                                                       \
+  hipLaunchKernelGGL((merge_uv_fixed_kernel<NT, OUT, SPL, 512, kParts, P, RT, AH>), dim3(H, rows, Z),     \
+                     dim3(64 * kParts * (2 / RT)), 0, st, B, H, dn, part_o, part_ml,                     \
+                     static_cast<const uint16_t*>(kv_b), static_cast<typename StoreT<OUT>::type*>(out))
+  if (blocks <= 64) MLA_MUF(2, 4, 1, 4);
+  else if (blocks <= 128) MLA_MUF(4, 2, 1, 4);
+  else MLA_MUF(8, 1, 2, 2);
 #undef MLA_MUF
 }
 
