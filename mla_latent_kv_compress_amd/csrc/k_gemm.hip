@@ -407,23 +407,22 @@ template <> struct Part8<uint16_t> {
   }
 };
 
-// NKH: the latent range is cut into NKH parts.  RT = 1: two waves per part, one per 16-row tile
-// (2 x NKH waves); RT = 2: one wave per part covering both row tiles (NKH waves), so W_UV is
-// requested once per work-group rather than once per row tile (the request stream, not the
-// bytes, bounds this kernel when every CU holds one work-group).  AH: K steps prefetched.
-// The d_v = 128 output columns are cut into 128 / (16 NT) blocks, one per blockIdx.z.
-template <int NT, int OUT, int SPL, int DC, int NKH, typename P, int RT, int AH>
-__global__ __launch_bounds__(64 * NKH * (2 / RT)) void merge_uv_fixed_kernel(
+// NKH: the latent range is cut into NKH parts, one wave per part covering both 16-row tiles
+// (RT), so W_UV is requested once per work-group rather than once per row tile (the request
+// stream, not the bytes, bounds this kernel).  AH: K steps prefetched.  The d_v = 128 output
+// columns are cut into 128 / (16 NT) blocks, one per blockIdx.z.
+template <int NT, int OUT, int SPL, int DC, int NKH, typename P, int AH>
+__global__ __launch_bounds__(64 * NKH) void merge_uv_fixed_kernel(
     int B, int H, int dn, const P* __restrict__ part_o, const float* __restrict__ part_ml,
     const uint16_t* __restrict__ kv_b, typename StoreT<OUT>::type* __restrict__ out) {
-  constexpr int dv = 128, half = DC / NKH, nk = half / 32;
+  constexpr int dv = 128, half = DC / NKH, nk = half / 32, RT = 2;
   const int vb = blockIdx.z * 16 * NT;               // this work-group's output columns [vb, vb + 16 NT)
   static_assert(nk >= AH, "prefetch depth within the K loop");
   __shared__ f32x4_t red[2][NKH - 1][NT][64];       // other parts' sums, [row tile][part][tile][lane]
   __shared__ float wts[32][SPL];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = RT == 1 ? (wave & 1) : 0;          // first row tile of this wave
-  const int kh = RT == 1 ? (wave >> 1) : wave;      // latent part
+  const int rg = 0;                                 // first row tile of this wave
+  const int kh = wave;                              // latent part
   const int h = blockIdx.x, b0 = blockIdx.y * 32;
   // Order of the requests: the merge statistics (every thread fetches its row's, tid & 31, so no
   // branch splits the loads), then the first AH steps of partials and weights, and only then the
@@ -569,18 +568,18 @@ static void launch_merge_uv_fixed(int B, int H, int dn, const P* part_o, const f
   constexpr int kParts = 4;
   const unsigned rows = unsigned((B + 31) / 32);
   // Few (head, 32-row) blocks (the Lite shape's 16 heads, a handful of long sequences): cut the
-  // output columns over 2 or 4 work-groups, each streaming that share of W_UV^h.  Every form
-  // runs one wave per latent quarter over both row tiles (RT = 2), measured faster than two
-  // waves per quarter in all three (17.0 -> 13.9, 9.6 -> 8.4 and 5.6 -> 5.3 us at the 236B,
-  // 128K and Lite decode workloads).
+  // output columns over 2 or 4 work-groups, each streaming that share of W_UV^h.  (One wave per
+  // latent quarter over both row tiles measured faster than two waves per quarter, one per row
+  // tile, in all three forms: 17.0 -> 13.9, 9.6 -> 8.4 and 5.6 -> 5.3 us at the 236B, 128K and
+  // Lite decode workloads.)
   const long blocks = long(H) * rows;
-#define MLA_MUF(NT, Z, RT, AH)                                                                       \
-  hipLaunchKernelGGL((merge_uv_fixed_kernel<NT, OUT, SPL, 512, kParts, P, RT, AH>), dim3(H, rows, Z),     \
-                     dim3(64 * kParts * (2 / RT)), 0, st, B, H, dn, part_o, part_ml,                     \
+#define MLA_MUF(NT, Z, AH)                                                                           \
+  hipLaunchKernelGGL((merge_uv_fixed_kernel<NT, OUT, SPL, 512, kParts, P, AH>), dim3(H, rows, Z),         \
+                     dim3(64 * kParts), 0, st, B, H, dn, part_o, part_ml,                                 \
                      static_cast<const uint16_t*>(kv_b), static_cast<typename StoreT<OUT>::type*>(out))
-  if (blocks <= 64) MLA_MUF(2, 4, 2, 2);
-  else if (blocks <= 128) MLA_MUF(4, 2, 2, 2);
-  else MLA_MUF(8, 1, 2, 2);
+  if (blocks <= 64) MLA_MUF(2, 4, 2);
+  else if (blocks <= 128) MLA_MUF(4, 2, 2);
+  else MLA_MUF(8, 1, 2);
 #undef MLA_MUF
 }
 
