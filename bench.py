@@ -1,24 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark: MLA decode step on one MI355X (236B-shaped layer, batch 64 x 8192 cached tokens).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-detail]
 
 A step is one mla_decode call: compress and append each new token, the query path with the
-k_nope absorption, split-K attention over the paged bf16 latent cache, the log-sum-exp merge
-and the v projection.  Inputs are seeded synthetic data already resident in HBM.  Prints one
-JSON line with whole-step throughput, the roofline of the dominant kernel (the attention,
-timed with HIP events recorded around it on the library's stream in a second pass over the
-same K steps, since an event record drains the stream and would inflate the throughput pass)
-and the fp64 CPU oracle timed on a bounded sample of the same workload.  Unless --no-prefill,
-detail.prefill also reports the chunked prefill of the mixed 236B workload (4 x 4096 prompt
-tokens, fp8 cache, chunks of 1024): prompt tokens/s and algorithmic MFMA TFLOP/s against the
-dense bf16 peak.
+k_nope absorption, split-K attention over the paged latent cache, the log-sum-exp merge and the
+v projection.  Inputs are seeded synthetic data already resident in HBM.
+
+Timing protocol: W untimed warm-up steps; then K steps, each preceded (outside its timed region)
+by a 512 MiB write to a scratch buffer that evicts the caches (the 256 MB Infinity Cache would
+otherwise hold the weights, and all of a small workload's cache, between steps); each step is
+bracketed by HIP events on the library's stream, and the line reports the median with p10 / p90.
+A second pass over the same K flushed steps records HIP events around the attention kernel
+alone (an event recorded inside the step costs a few microseconds of its own, so the two are
+separate passes); the dominant kernel's roofline uses that kernel's mean duration.  A third pass
+times K steps back to back between two synchronisations (caches warm), reported beside it.
+
+One JSON line: `value` is decode tokens/s of the whole step (B / median step time); `roofline`
+is the attention kernel's; `detail` holds the whole-step fractions, the other decode workloads
+(Lite 32 x 4096, 128K x 64 splits, the mixed fp8 ragged batch), the chunked prefill of the mixed
+workload, a stream bandwidth measured in the same run, the GPU, ROCm version, clocks and power;
+`cpu_baseline` is the fp64 oracle on a bounded sample of the headline workload.
 """
 import argparse
 import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -28,8 +37,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode tokens/s + achieved HBM GB/s & MFMA TFLOP/s (% roofline), 1 GPU"
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+FLUSH_BYTES = 512 << 20
 ATTN_SOURCE = os.path.join(ROOT, "mla_latent_kv_compress_amd", "csrc", "k_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_{}_traffic.json")
+DETAIL_WORKLOADS = ("lite_bf16", "dsv2_128k", "dsv2_mixed_fp8")
 
 
 def parse():
@@ -43,11 +54,209 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 1 GiB device copy (reference for hardware byte counters)")
-    p.add_argument("--graph", action="store_true",
-                   help="time the step as HIP-graph replays (the attention pass stays eager)")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the chunked-prefill measurement reported under detail.prefill")
+    p.add_argument("--no-detail", action="store_true",
+                   help="skip the other decode workloads reported under detail.decode")
+    p.add_argument("--no-flush", action="store_true", help="do not evict the caches between timed steps")
     return p.parse_args()
+
+
+def stats(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "mean": float(a.mean()), "n": int(a.size)}
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        path = "libamdhip64.so"
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]          # the runtime torch (and libmla) already use
+                break
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def smi_snapshot():
+    """Current shader / memory clock and socket power as rocm-smi reports them (None if absent)."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    out = {}
+    for card, vals in data.items():
+        if not isinstance(vals, dict):
+            continue
+        for k, v in vals.items():
+            kl = k.lower()
+            if "sclk" in kl or "mclk" in kl or "power" in kl or "fclk" in kl:
+                out[k] = v
+        break
+    return out or None
+
+
+def gpu_info(torch):
+    props = torch.cuda.get_device_properties(0)
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_gib": round(props.total_memory / 2 ** 30, 1),
+            "rocm_hip": torch.version.hip, "torch": torch.__version__}
+
+
+def stream_bandwidth(torch, nbytes=4 << 30, reps=5):
+    """Device copy of `nbytes` (read + write) and a read-only reduction over the same bytes."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    src.sum()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    cp, rd = [], []
+    for _ in range(reps):
+        e[0].record()
+        dst.copy_(src)
+        e[1].record()
+        s = src.sum()
+        e[2].record()
+        torch.cuda.synchronize()
+        cp.append(e[0].elapsed_time(e[1]))
+        rd.append(e[1].elapsed_time(e[2]))
+    del src, dst, s
+    torch.cuda.empty_cache()
+    return {"copy_gbps": 2 * nbytes / (min(cp) * 1e-3) / 1e9, "read_gbps": nbytes / (min(rd) * 1e-3) / 1e9,
+            "bytes": nbytes, "method": "torch device copy (read + write) and fp32 sum (read), best of 5"}
+
+
+def workload_work(wl, ctx):
+    """Algorithmic bytes and flops of one decode step: the attention core and the whole step."""
+    s = wl.shape
+    B = len(ctx)
+    H, D = s.num_heads, s.hidden_size
+    row_bytes = {"bf16": s.row_width * 2, "fp8": s.row_width + 4, "f32": s.row_width * 4}[wl.cache_dtype]
+    asz = 2 if wl.act_dtype == "bf16" else 4
+    n_ctx = float(sum(int(c) for c in ctx))
+    attn_bytes = n_ctx * row_bytes
+    attn_flops = n_ctx * 2 * H * (2 * s.kv_lora_rank + s.qk_rope_head_dim)
+    uk_uv = H * (s.qk_nope_head_dim + s.v_head_dim) * s.kv_lora_rank
+    qpath = (s.q_lora_rank * D + H * s.qk_head_dim * s.q_lora_rank) if s.q_lora_rank else H * s.qk_head_dim * D
+    kv_a = s.row_width * D
+    core_bytes = attn_bytes + uk_uv * asz
+    core_flops = attn_flops + B * 2.0 * uk_uv
+    step_bytes = core_bytes + (qpath + kv_a) * asz
+    step_flops = core_flops + B * 2.0 * (qpath + kv_a)
+    return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, core_bytes=core_bytes, core_flops=core_flops,
+                step_bytes=step_bytes, step_flops=step_flops)
+
+
+def measure_decode(name, steps, warmup, flush, splits=None, keep=False):
+    """Time one decode workload under the flushed per-step protocol (and back to back)."""
+    import numpy as np
+    import torch
+    from mla_latent_kv_compress_amd import api, configs
+    from mla_latent_kv_compress_amd.workload import DecodeBatch, Layer
+
+    wl = configs.WORKLOADS[name]
+    t_setup = time.perf_counter()
+    layer = Layer(wl.shape, wl.act_dtype, wl.cache_dtype, out_dtype="f32")
+    batch = DecodeBatch(layer, wl)
+    B = len(batch.hist)
+    max_blocks = batch.table.shape[1]
+    if splits is None:
+        splits = wl.num_splits or api.decode_num_splits(layer.cfg, B, max_blocks)
+    ws = torch.empty(api.decode_workspace_size(layer.cfg, B, max_blocks, splits), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, wl.shape.num_heads, wl.shape.v_head_dim), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if flush else None
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print(f"setup {setup_s:.1f} s: {name} B={B} splits={splits}", file=sys.stderr, flush=True)
+
+    def step(events=None):
+        batch.run(num_splits=splits, out=out, workspace=ws, attn_events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    # pass 1: whole steps, caches evicted before each (outside the events)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if flush:
+            scratch.fill_(i & 0xFF)
+        marks[i][0].record()
+        step()
+        marks[i][1].record()
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in marks]
+    # pass 2: the attention kernel alone, HIP events on the library's stream
+    pairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    for i in range(steps):
+        if flush:
+            scratch.fill_(i & 0xFF)
+        step(events=pairs[i])
+    torch.cuda.synchronize()
+    attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for e in [x for p in pairs for x in p]:
+        ev.destroy(e)
+    # pass 3: back to back, synchronised on both sides (caches warm between steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    b2b_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    ctx = batch.ctx.astype(np.int64)
+    work = workload_work(wl, ctx)
+    st, at = stats(step_ms), stats(attn_ms)
+    med_s, attn_mean_s = st["median"] * 1e-3, at["mean"] * 1e-3
+    bound_attn = "mfma (bf16)" if wl.cache_dtype == "fp8" else "hbm"
+    res = {
+        "workload": f"{name}: {wl.description}",
+        "batch": B, "max_ctx": int(ctx.max()), "sum_ctx": int(ctx.sum()), "num_splits": splits,
+        "cache_dtype": wl.cache_dtype, "setup_s": setup_s, "caches_evicted_between_steps": bool(flush),
+        "step_ms": st, "decode_tokens_per_s": B / med_s,
+        "back_to_back_ms_per_step": b2b_ms, "back_to_back_tokens_per_s": B / (b2b_ms * 1e-3),
+        "attn_ms": at,
+        "attn_alg_bytes": work["attn_bytes"], "attn_alg_flops": work["attn_flops"],
+        "attn_hbm_gbps": work["attn_bytes"] / attn_mean_s / 1e9,
+        "attn_hbm_frac": work["attn_bytes"] / attn_mean_s / 1e9 / HBM_PEAK_GBPS,
+        "attn_mfma_tflops": work["attn_flops"] / attn_mean_s / 1e12,
+        "attn_mfma_frac": work["attn_flops"] / attn_mean_s / 1e12 / BF16_PEAK_TFLOPS,
+        "attn_bound": bound_attn,
+        "step_alg_bytes": work["step_bytes"], "step_alg_flops": work["step_flops"],
+        "step_hbm_gbps": work["step_bytes"] / med_s / 1e9,
+        "step_hbm_frac": work["step_bytes"] / med_s / 1e9 / HBM_PEAK_GBPS,
+        "step_mfma_tflops": work["step_flops"] / med_s / 1e12,
+        "step_mfma_frac": work["step_flops"] / med_s / 1e12 / BF16_PEAK_TFLOPS,
+    }
+    if keep:
+        return res, (layer, batch)
+    del layer, batch, ws, out, scratch
+    torch.cuda.empty_cache()
+    return res, None
 
 
 def prefill_measure(passes=3):
@@ -88,6 +297,8 @@ def prefill_measure(passes=3):
         "attention": 2.0 * pairs * H * (s.qk_head_dim + s.v_head_dim),
     }
     total = sum(flops.values())
+    del layer, pb, ws, out
+    torch.cuda.empty_cache()
     return {
         "workload": f"dsv2_mixed_fp8 prefill: {wl.prefill_seqs} x {wl.prefill_len} tokens in chunks of "
                     f"{wl.prefill_chunk}, fp8 cache",
@@ -96,36 +307,6 @@ def prefill_measure(passes=3):
         "mfma_tflops": total / t / 1e12, "mfma_frac": total / t / 1e12 / BF16_PEAK_TFLOPS,
         "bound": "mfma (bf16)",
     }
-
-
-class HipEvents:
-    """hipEvent_t handles from the HIP runtime torch already loaded."""
-
-    def __init__(self):
-        path = "libamdhip64.so"
-        for line in open("/proc/self/maps"):
-            if "libamdhip64" in line:
-                path = line.split()[-1]          # the runtime torch (and libmla) already use
-                break
-        self.hip = ctypes.CDLL(path)
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-
-    def create(self):
-        ev = ctypes.c_void_p()
-        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        return ev.value
-
-    def elapsed_ms(self, a, b):
-        ms = ctypes.c_float()
-        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
-
-    def destroy(self, ev):
-        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
 def blas_threads():
@@ -137,6 +318,16 @@ def blas_threads():
     except Exception:
         pass
     return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(layer, batch, target_s):
@@ -168,6 +359,7 @@ def cpu_baseline(layer, batch, target_s):
         if timed >= target_s:
             break
     return {"value": n / timed, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"{n} of {len(batch.hist)} decode sequences (context {int(batch.ctx[0])}, all "
                       f"{s.num_heads} heads), fp64 numpy explicit form, {timed:.1f} s timed"}
 
@@ -180,145 +372,85 @@ def main():
               "sequences; see the design notes on sharding). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from mla_latent_kv_compress_amd import api, configs
-    from mla_latent_kv_compress_amd.workload import DecodeBatch, Layer
 
     api.lib()
     torch.cuda.set_device(0)
     wl = configs.WORKLOADS[args.workload]
     if wl.decode_batch <= 0:
         raise SystemExit(f"workload {args.workload} has no decode batch")
-    t_setup = time.perf_counter()
-    layer = Layer(wl.shape, wl.act_dtype, wl.cache_dtype, out_dtype="f32")
-    batch = DecodeBatch(layer, wl)
-    B = len(batch.hist)
-    max_blocks = batch.table.shape[1]
-    splits = args.splits if args.splits is not None else (wl.num_splits or api.decode_num_splits(layer.cfg, B, max_blocks))
-    ws = torch.empty(api.decode_workspace_size(layer.cfg, B, max_blocks, splits), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, wl.shape.num_heads, wl.shape.v_head_dim), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-    print(f"setup {setup_s:.1f} s: {args.workload} B={B} splits={splits}", file=sys.stderr, flush=True)
-
-    ev = HipEvents()
-
-    def attn_pass(steps):
-        """The same decode steps with HIP events recorded around the attention kernel."""
-        pairs = [(ev.create(), ev.create()) for _ in range(steps)]
-        torch.cuda.synchronize()
-        for i in range(steps):
-            batch.run(num_splits=splits, out=out, workspace=ws, attn_events=pairs[i])
-        torch.cuda.synchronize()
-        ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-        for e in [x for p in pairs for x in p]:
-            ev.destroy(e)
-        return ms
-
-    # Throughput pass: K plain steps (no event records: each record drains the stream for a few
-    # microseconds, which would inflate the step time).
-    if not args.graph:
-        for _ in range(args.warmup):
-            batch.run(num_splits=splits, out=out, workspace=ws)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            batch.run(num_splits=splits, out=out, workspace=ws)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-    else:
-        # One decode step captured as a HIP graph.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            batch.run(num_splits=splits, out=out, workspace=ws)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            batch.run(num_splits=splits, out=out, workspace=ws)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        del graph
-    # Attention pass: the same K steps again, eager, with the kernel bracketed by HIP events on
-    # the library's stream (the stream it is launched on).
-    attn_ms = attn_pass(args.steps)
-
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = B / (ms_per_step * 1e-3)
-    s = wl.shape
-    ctx = batch.ctx.astype(np.int64)
-    row_bytes = s.row_width * (2 if wl.cache_dtype == "bf16" else 1) + (4 if wl.cache_dtype == "fp8" else 0)
-    if wl.cache_dtype == "f32":
-        row_bytes = s.row_width * 4
-    attn_bytes = float(ctx.sum()) * row_bytes                      # algorithmic: each cached row once
-    attn_flops = float(ctx.sum()) * 2 * s.num_heads * (2 * s.kv_lora_rank + s.qk_rope_head_dim)
-    attn_avg_ms = float(np.mean(attn_ms))
-    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    flush = not args.no_flush
+    smi_before = smi_snapshot()
+    head, keep = measure_decode(args.workload, args.steps, args.warmup, flush, splits=args.splits,
+                                keep=not args.no_cpu_baseline)
+    smi_after_headline = smi_snapshot()
+    B = head["batch"]
 
     traffic = None
     tf = TRAFFIC_FILE.format(args.workload)
     if os.path.exists(tf):
         rec = json.load(open(tf))
         src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") == src and rec.get("splits") == splits:
+        if rec.get("kernel_source_sha256") == src and rec.get("splits") == head["num_splits"]:
             traffic = rec.get("bytes_per_launch")
 
-    # whole-step algorithmic bytes: cache rows + every weight matrix once (+ activations, small)
-    asz = 2 if wl.act_dtype == "bf16" else 4
-    H, D = s.num_heads, s.hidden_size
-    w_elems = (s.row_width * D + H * (s.qk_nope_head_dim + s.v_head_dim) * s.kv_lora_rank
-               + (s.q_lora_rank * D + H * s.qk_head_dim * s.q_lora_rank if s.q_lora_rank else H * s.qk_head_dim * D))
-    step_bytes = attn_bytes + w_elems * asz
-    line = {
-        "metric": METRIC,
-        "value": tokens_per_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.act_dtype,
-        "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {wl.description}", "global_batch": B,
-                   "seq_len": int(ctx.max()), "cache_dtype": wl.cache_dtype, "num_splits": splits,
-                   "parallelism": "single GPU", "launch": "hip_graph" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
-        "detail": {
-            "dominant_kernel": "decode_attn_latent_kernel (split-K attention over the latent cache)",
-            "attn_avg_ms": attn_avg_ms,
-            "attn_timing": "HIP events around the kernel on the library stream, second pass of the same steps",
-            "attn_alg_bytes": attn_bytes,
-            "attn_mfma_tflops": attn_flops / (attn_avg_ms * 1e-3) / 1e12,
-            "attn_mfma_frac": attn_flops / (attn_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "step_alg_bytes": step_bytes,
-            "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
-            "step_hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "setup_s": setup_s,
-        },
+    detail = {
+        "dominant_kernel": "decode_attn_latent_kernel (split-K attention over the latent cache)",
+        "headline": head,
+        "gpu": gpu_info(torch),
+        "clocks_power_before": smi_before,
+        "clocks_power_after_headline": smi_after_headline,
     }
+    try:
+        detail["stream"] = stream_bandwidth(torch)
+    except Exception as e:                        # measurement aid only
+        detail["stream"] = {"error": str(e)}
+    if not args.no_detail:
+        detail["decode"] = {}
+        for name in DETAIL_WORKLOADS:
+            if name == args.workload:
+                continue
+            res, _ = measure_decode(name, min(args.steps, 20), min(args.warmup, 3), flush)
+            detail["decode"][name] = res
     if not args.no_prefill:
-        line["detail"]["prefill"] = prefill_measure()
+        detail["prefill"] = prefill_measure()
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        line["detail"]["copy_calibration_bytes"] = 1 << 30
+        detail["copy_calibration_bytes"] = 1 << 30
         del src, dst
+    detail["clocks_power_after"] = smi_snapshot()
+
+    achieved = head["attn_hbm_gbps"]
+    stream_read = detail["stream"].get("read_gbps") if isinstance(detail.get("stream"), dict) else None
+    line = {
+        "metric": METRIC,
+        "value": head["decode_tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["step_ms"]["median"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.act_dtype,
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "global_batch": B, "seq_len": head["max_ctx"],
+                   "cache_dtype": wl.cache_dtype, "num_splits": head["num_splits"], "parallelism": "single GPU",
+                   "launch": "eager", "timing": "median of per-step HIP events, caches evicted between steps"},
+        "roofline": {"kernel": "decode_attn_latent_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "frac_of_measured_stream_read": (achieved / stream_read) if stream_read else None,
+                     "step_frac": head["step_hbm_frac"]},
+        "detail": detail,
+    }
     if not args.no_cpu_baseline:
+        layer, batch = keep
         line["cpu_baseline"] = cpu_baseline(layer, batch, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -43,11 +43,15 @@
  *                                           a multiple of 16, hidden_size and q_lora_rank
  *                                           multiples of 8
  * Precision of the bf16 path: weights, hidden states and the cache are read as stored;
- * products accumulate in fp32.  Decode scores the cache with the absorbed query rounded to
- * bf16 and weights the latents with bf16 probabilities; each split's softmax state is handed to
- * the merge in fp16 under a per-head power-of-two scale (11 significant bits of every entry
- * within 2^-29 of the head's largest); prefill rounds queries, decompressed
- * keys / values and probabilities to fp16 (all are of moderate range) before its MFMAs.
+ * products accumulate in fp32.  Decode carries the normed query latent and q_nope in fp32 into
+ * their projections (each as a bf16 hi + lo pair), scores the cache with the absorbed query's
+ * latent part in bf16 and its RoPE part in fp16 (the rotary key converted exactly), and weights
+ * the latents with bf16 probabilities; each split's softmax state is handed to the merge in fp16
+ * under a per-head power-of-two scale (11 significant bits of every entry within 2^-29 of the
+ * head's largest).  Prefill rounds the normed query latent, queries, decompressed keys / values
+ * and probabilities to fp16 before its MFMAs (q_b_proj enters as an fp16 copy, exact for
+ * magnitudes 2^-14 .. 65504; stores to fp16 saturate at +-65504); an fp8 cache enters the
+ * decompression as exact code values with the token scale applied in fp32.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -192,6 +196,20 @@ int mla_prefill(const mla_config *cfg, const mla_weights *w, const void *hidden,
                 int32_t max_blocks, const mla_cache *cache, int32_t num_seqs,
                 int32_t total_tokens, int32_t max_q_len, int32_t max_ctx, void *workspace,
                 size_t workspace_bytes, void *out, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * The fp8 cache's number format on the device (page "DeepSeek-V3.2-Exp 中多头潜在注意力的优化",
+ * deployment section: the latent is stored in fp8; the format taken is OCP e4m3fn).  These are
+ * the conversions mla_compress_append applies to (row value / token scale) and the attention
+ * kernels undo, exposed so a caller can fill or read an fp8 cache itself.
+ *   mla_fp8_e4m3_encode: codes[i] = nearest e4m3fn value of x[i], ties to even; magnitudes at or
+ *                        above 448 saturate to +-448 (0x7E / 0xFE); NaN gives 0x7F / 0xFF.
+ *   mla_fp8_e4m3_decode: x[i] = the value of codes[i] (exact in fp32); 0x7F / 0xFF give NaN.
+ *   n >= 0 elements (0 enqueues nothing); device pointers; asynchronous on `stream`.
+ * Returns MLA_ERR_INVALID_ARG for a null pointer with n > 0 or n < 0.
+ */
+int mla_fp8_e4m3_encode(const float *x, uint8_t *codes, int64_t n, void *stream);
+int mla_fp8_e4m3_decode(const uint8_t *codes, float *x, int64_t n, void *stream);
 
 /* Static text for a status code. */
 const char *mla_status_string(int status);

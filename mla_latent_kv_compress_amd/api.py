@@ -58,6 +58,8 @@ SIGNATURES = {
                                   _vp, _sz, _vp, _vp]),
     "mla_decode_timed": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                         _i32, _vp, _sz, _vp, _vp, _vp, _vp]),
+    "mla_fp8_e4m3_encode": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
+    "mla_fp8_e4m3_decode": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
     "mla_prefill_workspace_size": (_sz, [_P(MlaConfig), _i32, _i32, _i32, _i32]),
     "mla_prefill": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                    _i32, _i32, _i32, _vp, _sz, _vp, _vp]),

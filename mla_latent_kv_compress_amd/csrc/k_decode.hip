@@ -5,8 +5,10 @@
 // separate roles:
 //   score waves 0-3   wave w owns token tile w & 1 (16 tokens of each stage) and head half
 //                     w >> 1 (32 heads): S[token][head] = R . Qhat^T with
-//                     v_mfma_f32_16x16x32_bf16 (2 head tiles, 18 K steps over two accumulators
-//                     per tile), the query slice (144 registers) held for the whole split;
+//                     v_mfma_f32_16x16x32_bf16 over the latent and v_mfma_f32_16x16x32_f16 over
+//                     the RoPE part (the query's RoPE part is fp16, the key's converted exactly)
+//                     (2 head tiles, 18 K steps over two accumulators per tile), the query slice
+//                     (144 registers) held for the whole split;
 //                     softmax per head in base 2 (log2 e is folded into Qhat); P to LDS.
 //   value waves 4-7   wave 4+w owns latent columns [128w, 128w+128) for the 64 heads:
 //                     O^T[c][head] += R^T . P^T with v_mfma_f32_32x32x16_bf16 (4 column tiles x
@@ -183,6 +185,27 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 }
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
+
+// Eight bf16 values to fp16, exactly for magnitudes in [2^-14, 65504] (the RoPE key's range;
+// smaller ones lose at most 2^-24, larger ones saturate).
+__device__ __forceinline__ f16x8_t bf16x8_to_f16(bf16x8_t v) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  auto cv = [](uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                   __uint_as_float(w & 0xFFFF0000u)));
+  };
+  return __builtin_bit_cast(f16x8_t, make_uint4(cv(u.x), cv(u.y), cv(u.z), cv(u.w)));
+}
+
+// Eight e4m3 codes (two words, code j in byte j) to eight fp16 values, exactly.
+__device__ __forceinline__ f16x8_t fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(w0), 1.0f, false);
+  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(w0), 1.0f, true);
+  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(w1), 1.0f, false);
+  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(w1), 1.0f, true);
+  return f16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 // Eight e4m3 codes (two words, code j in byte j) to eight bf16 values, exactly.
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -459,13 +482,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
         const int mn = m + kR - 1;
         if (mn < kM) raw[mn % kR] = score_raw(st, mn);
         const uint4 r = raw[m % kR];
-        const bf16x8_t a0 = fp8x8_to_bf16(r.x, r.y), a1 = fp8x8_to_bf16(r.z, r.w);
+        if (m < kM - 1) {                                 // latent: bf16 products
+          const bf16x8_t a0 = fp8x8_to_bf16(r.x, r.y), a1 = fp8x8_to_bf16(r.z, r.w);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[nt][2 * m], s[nt][0], 0, 0, 0);
+          for (int nt = 0; nt < 2; ++nt)
+            s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[nt][2 * m], s[nt][0], 0, 0, 0);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[nt][2 * m + 1], s[nt][1], 0, 0, 0);
+          for (int nt = 0; nt < 2; ++nt)
+            s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[nt][2 * m + 1], s[nt][1], 0, 0, 0);
+        } else {                                          // RoPE part: fp16 products
+          const f16x8_t a0 = fp8x8_to_f16(r.x, r.y), a1 = fp8x8_to_f16(r.z, r.w);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(f16x8_t, qf[nt][2 * m]), s[nt][0], 0, 0, 0);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(f16x8_t, qf[nt][2 * m + 1]), s[nt][1], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       return;
@@ -477,9 +510,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     for (int ks = 0; ks < kKS; ++ks) {
       const int kn = ks + kScoreRing - 1;
       if (kn < kKS) a[kn % kScoreRing] = score_a(st, kn);
+      if (ks < kDC / 32) {                       // latent: bf16 products
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        s[nt][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks % kScoreRing], qf[nt][ks], s[nt][ks & 1], 0, 0, 0);
+        for (int nt = 0; nt < 2; ++nt)
+          s[nt][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks % kScoreRing], qf[nt][ks], s[nt][ks & 1], 0, 0, 0);
+      } else {                                   // RoPE part: the key converted to fp16, fp16 products
+        const f16x8_t ah = bf16x8_to_f16(a[ks % kScoreRing]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          s[nt][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(f16x8_t, qf[nt][ks]), s[nt][ks & 1], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);        // keep the source order: reads stay ahead of use
     }
   };

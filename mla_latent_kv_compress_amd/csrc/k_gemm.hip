@@ -178,16 +178,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
 // each work-group owns 64 or 96 output columns and streams its [columns x K-chunk] slice of W
 // (and the matching slice of X, an L2 hit) through a ring of LDS stages with direct
 // global->LDS loads, several stages ahead of the MFMAs.  A stage is 64 k of X (MR = 64 or 128
-// rows) and of W,
-// rows of 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), so the 16 rows
-// of an MFMA operand read fall on distinct banks.  Rows past M (or N) re-read the last valid
-// row; their outputs are not stored.  Requires K and the K chunk to be multiples of 64.
+// rows) and of W.  bf16 rows are 128 bytes with 16-byte chunk c of row r stored at
+// c ^ ((r >> 1) & 7), so the 16 rows of an MFMA operand read fall on distinct banks.  With XF
+// the activation X is fp32 (rows of 256 bytes, chunk c of row r at c ^ (r & 15)) and enters the
+// matrix core as a bf16 pair hi = bf16(x), lo = bf16(x - hi): two products per fragment, so the
+// activation is carried to about 2^-16 of its value instead of bf16's 2^-9.  Rows past M (or N)
+// re-read the last valid row; their outputs are not stored.  Requires K and the K chunk to be
+// multiples of 64.
 namespace {
-template <int BN, int MR> constexpr int sk_stage_bytes() { return (MR + BN) * 128; }
-// Ring depth: 4 stages (16 to 28 KiB each), three stages of loads in flight.  (Measured: a
-// 7-stage ring for the one-per-CU 96-column tiles made the 236B-shaped q_b and kv_a + q_a
-// projections slower, not faster.)
-template <int BN> constexpr int sk_stages() { return 4; }
+template <int BN, int MR, bool XF = false> constexpr int sk_stage_bytes() { return MR * (XF ? 256 : 128) + BN * 128; }
+// Ring depth: 4 stages (16 to 40 KiB each), three stages of loads in flight; 3 when four stages
+// would not fit the 160 KiB of LDS (the 128-row fp32 activation tile).  (Measured: a 7-stage
+// ring for the one-per-CU 96-column tiles made the 236B-shaped q_b and kv_a + q_a projections
+// slower, not faster.)
+template <int BN, int MR = 64, bool XF = false> constexpr int sk_stages() {
+  return 4 * sk_stage_bytes<BN, MR, XF>() <= 160 * 1024 ? 4 : 3;
+}
 
 __device__ __forceinline__ void sk_dma16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
@@ -210,7 +216,7 @@ __device__ __forceinline__ void sk_barrier() {
 // One skinny problem: Y[z / nsplit] (+ split z % nsplit) = alpha X W^T over the split's K chunk.
 struct SkinnyProb {
   int M, N, K, kchunk, nsplit;
-  const uint16_t* X;
+  const void* X;             // bf16, or fp32 (entering the products as a bf16 hi + lo pair)
   long lda, sx;
   const uint16_t* W;
   long ldw, sw;
@@ -221,25 +227,25 @@ struct SkinnyProb {
 };
 
 // Output mode of the decode query projection (q_b, N = H x 192): columns 0..127 of each head
-// (q_nope) are stored as bf16(alpha q) to Y [M][H][128], the A operand the absorb kernel feeds
-// straight to the matrix core, and columns 128..191 (q_pe) as fp32 q to Y2 [M][H][64], which
-// the absorb kernel rotates.  This is the rounding that kernel applies to the fp32 projection.
+// (q_nope) are stored as fp32 alpha q to Y [M][H][128], which the absorb kernel feeds to the
+// matrix core as a bf16 hi + lo pair, and columns 128..191 (q_pe) as fp32 q to Y2 [M][H][64],
+// which the absorb kernel rotates.
 constexpr int kOutQSplit = 7;
 
 // Output tile (MR rows x BN columns from column tile nx) of batch-and-split index z.  BN is 64 or
-// 96, MR 64 or 128: a stage holds the X tile (MR rows x 64 k) and the W tile (BN rows x 64 k),
-// rows of 128 bytes, (MR + BN) / 8 direct-load instructions of 1 KiB (8 rows each) dealt
-// round-robin to the four waves; wave (wm, wn) computes rows MR / 2 wm .. + MR / 2 and columns
-// BN / 2 wn .. + BN / 2.
-template <int OUT, int BN, int MR>
+// 96, MR 64 or 128: a stage holds the X tile (MR rows x 64 k) and the W tile (BN rows x 64 k);
+// whole KiBs of it are filled by one direct-load instruction each (8 bf16 rows of 128 bytes, or
+// 4 fp32 rows of 256 bytes), dealt round-robin to the four waves; wave (wm, wn) computes rows
+// MR / 2 wm .. + MR / 2 and columns BN / 2 wn .. + BN / 2.
+template <int OUT, int BN, int MR, bool XF = false>
 __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, char* ring) {
-  constexpr int kStageB = sk_stage_bytes<BN, MR>();
-  constexpr int S = sk_stages<BN>();
-  constexpr int NQ = (MR + BN) / 8 / 4;                  // load instructions per wave per stage
+  constexpr int kStageB = sk_stage_bytes<BN, MR, XF>();
+  constexpr int S = sk_stages<BN, MR, XF>();
+  constexpr int XK = MR * (XF ? 256 : 128) / 1024;       // KiBs of the stage that hold X
+  constexpr int NQ = (XK + BN / 8) / 4;                  // load instructions per wave per stage
   constexpr int NC = BN / 32;                            // 16-column tiles per wave
   constexpr int MT = MR / 32;                            // 16-row tiles per wave
-  constexpr int XK = MR / 8;                             // KiBs of the stage that hold X
-  static_assert((MR + BN) % 32 == 0, "whole instructions per wave");
+  static_assert((XK + BN / 8) % 4 == 0, "whole instructions per wave");
   const int M = p.M, N = p.N, K = p.K, kchunk = p.kchunk, nsplit = p.nsplit;
   const long lda = p.lda, ldw = p.ldw, ldc = p.ldc;
   const float alpha = p.alpha;
@@ -247,32 +253,45 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int b = z / nsplit, sp = z % nsplit;
-  const uint16_t* X = p.X + b * p.sx;
+  const char* X = reinterpret_cast<const char*>(p.X) + b * p.sx * (XF ? 4 : 2);
   const uint16_t* W = p.W + b * p.sw;
   typename StoreT<OUT>::type* Y = static_cast<typename StoreT<OUT>::type*>(p.Y) + b * p.sy + sp * p.ssplit;
   const int k0 = sp * kchunk;
   const int nk = (min(K, k0 + kchunk) - k0) / 64;      // 64-wide K steps of this split
   const int n0 = nx * BN;
 
-  // Instruction q = wave + 4 j fills KiB q of the stage: q < XK are X rows 8q .. +7, the rest W
-  // rows 8 (q - XK) .. +7 (lane i -> row + (i >> 3), stored chunk i & 7).
+  // Instruction q = wave + 4 j fills KiB q of the stage: q < XK are X rows (bf16: 8q .. +7, lane
+  // i -> row + (i >> 3), stored chunk i & 7; fp32: 4q .. +3, lane i -> row + (i >> 4), stored
+  // chunk i & 15), the rest W rows 8 (q - XK) .. +7 (lane i -> row + (i >> 3), stored chunk i & 7).
   uint32_t off[NQ];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int q = wave + 4 * j;
-    const bool isx = q < XK;
-    const int r = 8 * (isx ? q : q - XK) + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    off[j] = isx ? uint32_t((long(min(r, M - 1)) * lda + 8 * c) * 2) : uint32_t((long(min(n0 + r, N - 1)) * ldw + 8 * c) * 2);
+    if (q < XK) {
+      if constexpr (XF) {
+        const int r = 4 * q + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        off[j] = uint32_t((long(min(r, M - 1)) * lda + 4 * c) * 4);
+      } else {
+        const int r = 8 * q + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        off[j] = uint32_t((long(min(r, M - 1)) * lda + 8 * c) * 2);
+      }
+    } else {
+      const int r = 8 * (q - XK) + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      off[j] = uint32_t((long(min(n0 + r, N - 1)) * ldw + 8 * c) * 2);
+    }
   }
   auto issue = [&](int jj) {
     if (jj >= nk) return;
     char* st = ring + (jj % S) * kStageB;
-    const long kb = long(k0 + 64 * jj) * 2;
+    const long kb = long(k0 + 64 * jj);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int q = wave + 4 * j;                       // uniform: q < XK selects X
-      sk_dma16(reinterpret_cast<const char*>(q < XK ? X : W) + kb, off[j], sk_lds_addr(st + q * 1024));
+      sk_dma16(q < XK ? X + kb * (XF ? 4 : 2) : reinterpret_cast<const char*>(W) + kb * 2, off[j],
+               sk_lds_addr(st + q * 1024));
     }
   };
   auto wait_for = [&](int jj) {                         // stage jj landed (this wave's part)
@@ -282,7 +301,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
       case 5: sk_wait_vm<(S >= 7 ? 5 : 0) * NQ>(); break;
       case 4: sk_wait_vm<(S >= 6 ? 4 : 0) * NQ>(); break;
       case 3: sk_wait_vm<(S >= 5 ? 3 : 0) * NQ>(); break;
-      case 2: sk_wait_vm<2 * NQ>(); break;
+      case 2: sk_wait_vm<(S >= 4 ? 2 : 0) * NQ>(); break;
       case 1: sk_wait_vm<NQ>(); break;
       default: sk_wait_vm<0>(); break;
     }
@@ -308,20 +327,43 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     sk_barrier();                                       // stage i visible; stage i - 1 consumed
     issue(i + S - 1);
     const char* st = ring + (i % S) * kStageB;
+    constexpr int kXB = XF ? 256 : 128;                 // X row bytes
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8_t af[MT], bf[NC];
+      [[maybe_unused]] bf16x8_t al[MT];
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
-        af[t] = *reinterpret_cast<const bf16x8_t*>(st + arow[t] * 128 + 16 * ((4 * kk + g) ^ ((arow[t] >> 1) & 7)));
+      for (int t = 0; t < MT; ++t) {
+        if constexpr (XF) {                             // 8 fp32 values: stored chunks of 2 (4kk + g), + 1
+          const char* row = st + arow[t] * kXB;
+          const int sw = arow[t] & 15;
+          const float4 x0 = *reinterpret_cast<const float4*>(row + 16 * ((8 * kk + 2 * g) ^ sw));
+          const float4 x1 = *reinterpret_cast<const float4*>(row + 16 * ((8 * kk + 2 * g + 1) ^ sw));
+          const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+          bf16x8v hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            hi[e] = (__bf16)v[e];                       // round to nearest even
+            lo[e] = (__bf16)(v[e] - (float)hi[e]);
+          }
+          af[t] = __builtin_bit_cast(bf16x8_t, hi);
+          al[t] = __builtin_bit_cast(bf16x8_t, lo);
+        } else {
+          af[t] = *reinterpret_cast<const bf16x8_t*>(st + arow[t] * 128 + 16 * ((4 * kk + g) ^ ((arow[t] >> 1) & 7)));
+        }
+      }
 #pragma unroll
       for (int t = 0; t < NC; ++t)
-        bf[t] = *reinterpret_cast<const bf16x8_t*>(st + MR * 128 + brow[t] * 128 +
+        bf[t] = *reinterpret_cast<const bf16x8_t*>(st + MR * kXB + brow[t] * 128 +
                                                    16 * ((4 * kk + g) ^ ((brow[t] >> 1) & 7)));
 #pragma unroll
       for (int a = 0; a < MT; ++a)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) {
+          acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bf[c], acc[a][c], 0, 0, 0);
+          if constexpr (XF) acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[a], bf[c], acc[a][c], 0, 0, 0);
+        }
     }
   }
   // C layout: lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile.
@@ -337,7 +379,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
           if constexpr (OUT == kOutQSplit) {
             const int hh = gn / 192, cc = gn - 192 * hh, HH = N / 192;
             if (cc < 128)
-              reinterpret_cast<uint16_t*>(p.Y)[(long(gm) * HH + hh) * 128 + cc] = f2bf(alpha * acc[a][c][r]);
+              reinterpret_cast<float*>(p.Y)[(long(gm) * HH + hh) * 128 + cc] = alpha * acc[a][c][r];
             else
               p.Y2[(long(gm) * HH + hh) * 64 + cc - 128] = acc[a][c][r];
           } else {
@@ -348,17 +390,17 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     }
 }
 
-template <int OUT, int BN, int MR>
+template <int OUT, int BN, int MR, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyProb p) {
-  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN, MR>()];
-  skinny_tile<OUT, BN, MR>(p, blockIdx.x, blockIdx.z, ring);
+  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN, MR, XF>() * sk_stage_bytes<BN, MR, XF>()];
+  skinny_tile<OUT, BN, MR, XF>(p, blockIdx.x, blockIdx.z, ring);
 }
 
 // Two independent skinny problems in one launch: work-groups [0, tiles0) take p0's tiles,
 // the rest p1's (one launch instead of two dependent-free ones back to back).
 template <int OUT, int BN, int MR>
 __global__ __launch_bounds__(256) void gemm_skinny_pair_kernel(SkinnyProb p0, SkinnyProb p1, int tiles0) {
-  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN>() * sk_stage_bytes<BN, MR>()];
+  __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN, MR>() * sk_stage_bytes<BN, MR>()];
   const int id = blockIdx.x;
   if (id < tiles0) {
     const int nx = (p0.N + BN - 1) / BN;
@@ -609,32 +651,40 @@ bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, 
 }
 
 // ------------------------------------------------------------------ absorb + query RoPE (decode)
-// qhat[b][h] = [ W_UK^h^T bf16(scale q_nope[b][h]) | bf16(scale RoPE(q_pe[b][h])) ] from the fp32
-// query projection (K-split partials summed in order).  W_UK^h is rows [h (dn + dv), +dn) of
-// kv_b_proj ([d][c], c contiguous): a work-group stages a [dn x 64] column block of it in LDS and
-// reads it with the transposing ds_read_b64_tr_b16 as the B operand (8 consecutive d per lane);
-// the A operand (64 decode rows x 32 d) comes straight from the fp32 projection.  The extra
-// column block blockIdx.x = dc / 64 applies RoPE to q_pe with the token angles in rope_tab.
-// QS: the query comes split by the projection's epilogue (q_nope as bf16(scale q) [B][H][DN],
-// q_pe as fp32 [B][H][dr]) instead of as fp32 partials; the products and roundings are the same.
+// qhat[b][h] = [ W_UK^h^T q_nope[b][h] (bf16, d_c values) | RoPE(q_pe[b][h]) (fp16, d_r values) ]
+// with the softmax scale (times log2 e) folded in.  W_UK^h is rows [h (dn + dv), +dn) of
+// kv_b_proj ([d][c], c contiguous).  Grid (3, H, ceil(B / 64)): blocks x = 0, 1 take latent
+// columns [256 x, 256 x + 256) for 64 decode rows, x = 2 rotates q_pe.  A latent block stages
+// its [128 d x 256 c] slice of W_UK^h in LDS (rows of 512 bytes, 32-byte segment s of row d at
+// s ^ (d & 15), so the transposing reads of 16 rows hit distinct banks) and reads it with
+// ds_read_b64_tr_b16 as the B operand (8 consecutive d per lane); wave w owns columns
+// 256 x + 64 w .. + 64 and keeps those B fragments in registers while it walks the four 16-row
+// tiles.  The query q_nope (fp32) enters the products as a bf16 pair hi + lo (two MFMAs per
+// fragment), so the latent query carries no bf16 rounding of its input; only the result is
+// rounded (to bf16).  The RoPE part is kept in fp16 (11 significant bits): with the rotary key
+// it scores in an fp16 product, where it would lose three bits in bf16.
+// QS: q_nope arrives as fp32 alpha q [B][H][DN] and q_pe as fp32 q [B][H][dr] (the projection's
+// split epilogue); otherwise q is the sum of nsplit fp32 partials of the projection.
 template <int DN, bool QS>
 __global__ __launch_bounds__(256) void absorb_rope_kernel(
     int B, int H, int dr, int dc, int dv, int nsplit, const float* __restrict__ q_acc,
-    const uint16_t* __restrict__ q_nope16, const float* __restrict__ q_pe32,
+    const float* __restrict__ q_nope32, const float* __restrict__ q_pe32,
     const float* __restrict__ rope_tab, float scale, const uint16_t* __restrict__ kv_b,
     uint16_t* __restrict__ qhat) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[DN * 64];
+  constexpr int kCols = 256;                          // latent columns per block
+  constexpr int kKs = DN / 32;                        // K steps
+  __shared__ __attribute__((aligned(16))) char wt[DN * kCols * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b0 = blockIdx.z * 64;
-  const int dqk = DN + dr;
+  const int dqk = DN + dr, W = dc + dr;
   const long nq = long(H) * dqk, sstride = long(B) * nq;
-  const float* qh = q_acc + long(h) * dqk;
+  const float* qh = q_acc + long(h) * dqk;            // (!QS) partial 0 of head h, row 0
   auto qsum = [&](int b, int i) {
     float v = 0.f;
     for (int sp = 0; sp < nsplit; ++sp) v += qh[sp * sstride + long(b) * nq + i];
     return v;
   };
-  if (blockIdx.x * 64 >= dc) {                        // RoPE block
+  if (blockIdx.x == 2) {                              // RoPE block: fp16 (scale RoPE(q_pe))
     const int half = dr / 2;
     for (int e = tid; e < 64 * half; e += 256) {
       const int b = b0 + e / half, pi = e % half;
@@ -642,92 +692,129 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
       const float c = rope_tab[long(b) * dr + pi], sn = rope_tab[long(b) * dr + half + pi];
       const float* qp = q_pe32 + (long(b) * H + h) * dr + 2 * pi;
       const float ev = QS ? qp[0] : qsum(b, DN + 2 * pi), ov = QS ? qp[1] : qsum(b, DN + 2 * pi + 1);
-      uint16_t* o = qhat + (long(b) * H + h) * (dc + dr) + dc + 2 * pi;
-      o[0] = f2bf(scale * (ev * c - ov * sn));
-      o[1] = f2bf(scale * (ev * sn + ov * c));
+      const uint32_t pr = uint32_t(f2h(scale * (ev * c - ov * sn))) | (uint32_t(f2h(scale * (ev * sn + ov * c))) << 16);
+      *reinterpret_cast<uint32_t*>(qhat + (long(b) * H + h) * W + dc + 2 * pi) = pr;
     }
     return;
   }
-  const int c0 = blockIdx.x * 64;
+  const int c0 = blockIdx.x * kCols;
   {
+    // W_UK^h[d][c0 .. c0 + 256): 16-byte chunk ch of row d (columns 8 ch .. + 7) at segment
+    // (ch >> 1) ^ (d & 15), half ch & 1
     const uint16_t* wsrc = kv_b + long(h) * (DN + dv) * dc + c0;
-    for (int k = tid; k < DN * 8; k += 256) {
-      const int row = k >> 3, cc = k & 7;
-      *reinterpret_cast<uint4*>(&wt[row * 64 + 8 * cc]) =
-          *reinterpret_cast<const uint4*>(wsrc + long(row) * dc + 8 * cc);
+    constexpr int kChunks = DN * kCols / 8;
+    uint4 v[kChunks / 256];
+#pragma unroll
+    for (int j = 0; j < kChunks / 256; ++j) {
+      const int i = tid + 256 * j, d = i >> 5, ch = i & 31;
+      v[j] = *reinterpret_cast<const uint4*>(wsrc + long(d) * dc + 8 * ch);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunks / 256; ++j) {
+      const int i = tid + 256 * j, d = i >> 5, ch = i & 31;
+      *reinterpret_cast<uint4*>(wt + d * 512 + 32 * ((ch >> 1) ^ (d & 15)) + 16 * (ch & 1)) = v[j];
     }
   }
   __syncthreads();
   const int li = lane & 15, g = lane >> 4;
-  const int b = b0 + 16 * wave + li;
-  f32x4_t acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // fp32 partials: every K step's values of one split are requested together, so the sum takes
-  // one round trip per split (the splits are added in order).
-  constexpr int kKs = DN / 32;
-  float v[kKs][8];
+  // B fragments of the wave's four 16-column tiles, all K steps: W_UK[32 ks + 8 g + j][c] for
+  // c = 64 wave + 16 nt + li: transposing reads of rows d0 .. d0 + 3 (and + 4 .. + 7), lane
+  // (li & 3) taking columns 4 (li & 3) .. + 3 of the tile's segment.
+  bf16x8_t bw[kKs][4];
 #pragma unroll
   for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[ks][j] = 0.f;
-  if (!QS && b < B) {
-    const float* src = qh + long(b) * nq + 8 * g;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      float4 x[kKs][2];
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        x[ks][0] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks);
-        x[ks][1] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks + 4);
-      }
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        v[ks][0] += x[ks][0].x; v[ks][1] += x[ks][0].y; v[ks][2] += x[ks][0].z; v[ks][3] += x[ks][0].w;
-        v[ks][4] += x[ks][1].x; v[ks][5] += x[ks][1].y; v[ks][6] += x[ks][1].z; v[ks][7] += x[ks][1].w;
-      }
-    }
-  }
-#pragma unroll
-  for (int ks = 0; ks < kKs; ++ks) {
-    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-    bf16x8v a;
-    if constexpr (QS) {
-      a = __builtin_bit_cast(bf16x8v, *reinterpret_cast<const bf16x8_t*>(
-                                          q_nope16 + (long(min(b, B - 1)) * H + h) * DN + 32 * ks + 8 * g));
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = (__bf16)(scale * v[ks][j]);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int nt = 0; nt < 4; ++nt) {
       typedef short s16x4v __attribute__((ext_vector_type(4)));
-      const uint16_t* p0 = &wt[(32 * ks + 8 * g + (li >> 2)) * 64 + 16 * t + 4 * (li & 3)];
+      const int d0 = 32 * ks + 8 * g + (li >> 2), seg = 4 * wave + nt;
+      const char* p0 = wt + d0 * 512 + 32 * (seg ^ (d0 & 15)) + 8 * (li & 3);
+      const char* p1 = wt + (d0 + 4) * 512 + 32 * (seg ^ ((d0 + 4) & 15)) + 8 * (li & 3);
       const s16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p0));
-      const s16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p0 + 4 * 64));
+      const s16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p1));
       typedef short s16x8v __attribute__((ext_vector_type(8)));
       const s16x8v bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv), acc[t], 0, 0, 0);
+      bw[ks][nt] = __builtin_bit_cast(bf16x8_t, bv);
     }
+  typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+#pragma unroll 1
+  for (int mt = 0; mt < 4; ++mt) {
+    const int b = b0 + 16 * mt + li;
+    if (b0 + 16 * mt >= B) break;                     // uniform over the wave
+    const int bl = min(b, B - 1);
+    float v[kKs][8];
+    if constexpr (QS) {
+      const float* src = q_nope32 + (long(bl) * H + h) * DN + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        const float4 x0 = *reinterpret_cast<const float4*>(src + 32 * ks);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 32 * ks + 4);
+        v[ks][0] = x0.x; v[ks][1] = x0.y; v[ks][2] = x0.z; v[ks][3] = x0.w;
+        v[ks][4] = x1.x; v[ks][5] = x1.y; v[ks][6] = x1.z; v[ks][7] = x1.w;
+      }
+    } else {
+      // fp32 partials: every K step's values of one split are requested together (one round
+      // trip per split; the splits are added in order), then scaled
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[ks][j] = 0.f;
+      const float* src = qh + long(bl) * nq + 8 * g;
+      for (int sp = 0; sp < nsplit; ++sp) {
+        float4 x[kKs][2];
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+          x[ks][0] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks);
+          x[ks][1] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks + 4);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+          v[ks][0] += x[ks][0].x; v[ks][1] += x[ks][0].y; v[ks][2] += x[ks][0].z; v[ks][3] += x[ks][0].w;
+          v[ks][4] += x[ks][1].x; v[ks][5] += x[ks][1].y; v[ks][6] += x[ks][1].z; v[ks][7] += x[ks][1].w;
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[ks][j] *= scale;
+    }
+    f32x4_t acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      bf16x8v hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hi[j] = (__bf16)v[ks][j];                       // round to nearest even
+        lo[j] = (__bf16)(v[ks][j] - (float)hi[j]);
+      }
+      const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, hi), al = __builtin_bit_cast(bf16x8_t, lo);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[ks][nt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[ks][nt], acc[nt], 0, 0, 0);
+      }
+    }
+    // C layout: lane holds C[4 g + r][li] of each 16 x 16 tile.
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int bo = b0 + 16 * mt + 4 * g + r;
+        if (bo < B) qhat[(long(bo) * H + h) * W + c0 + 64 * wave + 16 * nt + li] = f2bf(acc[nt][r]);
+      }
   }
-  // C layout: lane holds C[4 (lane / 16) + r][lane % 16] of each 16 x 16 tile.
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int bo = b0 + 16 * wave + 4 * g + r;
-      if (bo < B) qhat[(long(bo) * H + h) * (dc + dr) + c0 + 16 * t + li] = f2bf(acc[t][r]);
-    }
 }
 
 bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit, const float* q_acc,
                         const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st,
-                        const void* q_nope16, const float* q_pe32) {
-  if (dn != 128 || dc % 64 != 0 || dr % 2 != 0 || B <= 0) return false;
-  dim3 grid(dc / 64 + 1, H, (B + 63) / 64);
-  if (q_nope16 && q_pe32)
+                        const float* q_nope32, const float* q_pe32) {
+  if (dn != 128 || dc != 512 || dr % 2 != 0 || B <= 0) return false;
+  dim3 grid(3, H, (B + 63) / 64);
+  if (q_nope32 && q_pe32)
     hipLaunchKernelGGL((absorb_rope_kernel<128, true>), grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, nullptr,
-                       static_cast<const uint16_t*>(q_nope16), q_pe32, rope_tab, scale,
-                       static_cast<const uint16_t*>(kv_b), static_cast<uint16_t*>(qhat));
+                       q_nope32, q_pe32, rope_tab, scale, static_cast<const uint16_t*>(kv_b),
+                       static_cast<uint16_t*>(qhat));
   else
     hipLaunchKernelGGL((absorb_rope_kernel<128, false>), grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, q_acc,
                        nullptr, nullptr, rope_tab, scale, static_cast<const uint16_t*>(kv_b),
@@ -749,15 +836,18 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
 // The skinny kernel's conditions: TN, M <= 128, K and the chunk in 64-steps, 16-byte rows, and
 // per-operand offsets that fit the 32-bit load offsets.
 static bool skinny_ok(const GemmArgs& g) {
+  const long xs = g.xf32 ? 4 : 2;
   return g.kind == GEMM_BF16 && !g.nn && g.M <= 128 && g.K % 64 == 0 && g.kchunk % 64 == 0 &&
-         g.lda % 8 == 0 && g.ldw % 8 == 0 && long(g.M) * g.lda * 2 < (1L << 32) &&
+         g.lda % (16 / xs) == 0 && g.ldw % 8 == 0 && long(g.M) * g.lda * xs < (1L << 32) &&
          long(g.N) * g.ldw * 2 < (1L << 32);
 }
+
+bool launch_gemm_skinny_ok(const GemmArgs& g) { return skinny_ok(g); }
 
 static SkinnyProb skinny_prob(const GemmArgs& g) {
   SkinnyProb p;
   p.M = g.M; p.N = g.N; p.K = g.K; p.kchunk = g.kchunk; p.nsplit = g.nsplit;
-  p.X = static_cast<const uint16_t*>(g.X); p.lda = g.lda; p.sx = g.sx;
+  p.X = g.X; p.lda = g.lda; p.sx = g.sx;
   p.W = static_cast<const uint16_t*>(g.W); p.ldw = g.ldw; p.sw = g.sw;
   p.Y = g.Y; p.ldc = g.ldc; p.sy = g.sy; p.ssplit = g.ssplit;
   p.alpha = g.alpha;
@@ -765,25 +855,32 @@ static SkinnyProb skinny_prob(const GemmArgs& g) {
   return p;
 }
 
+// A skinny launch: 96-column tiles when they fill the CUs in whole rounds and 64-column tiles do
+// not (fewer, better balanced work-groups, each re-reading X for more columns).
+template <int OUT, bool XF>
+static void launch_skinny(const GemmArgs& g, const SkinnyProb& p, hipStream_t st) {
+  const long z = long(g.batch) * g.nsplit;
+#define MLA_SK(BN, MR, NX) \
+  hipLaunchKernelGGL((gemm_skinny_kernel<OUT, BN, MR, XF>), dim3(NX, 1, unsigned(z)), dim3(256), 0, st, p)
+  if (g.N % 96 == 0 && (g.N / 96) * z % 256 == 0 && ((g.N + 63) / 64) * z % 256 != 0) {
+    if (g.M <= 64) MLA_SK(96, 64, g.N / 96);
+    else MLA_SK(96, 128, g.N / 96);
+    return;
+  }
+  if (g.M <= 64) MLA_SK(64, 64, (g.N + 63) / 64);
+  else MLA_SK(64, 128, (g.N + 63) / 64);
+#undef MLA_SK
+}
+
 template <bool NN, int OUT>
 static void launch_bf16_shape(const GemmArgs& g, hipStream_t st) {
   long tiles_big = long((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch * g.nsplit;
-  if (skinny_ok(g)) {
-    // 96-column tiles when they fill the CUs in whole rounds and 64-column tiles do not (fewer,
-    // better balanced work-groups, each re-reading X for more columns)
-    const long z = long(g.batch) * g.nsplit;
-#define MLA_SK(BN, MR, NX) \
-  hipLaunchKernelGGL((gemm_skinny_kernel<OUT, BN, MR>), dim3(NX, 1, unsigned(z)), dim3(256), 0, st, skinny_prob(g))
-    if (g.N % 96 == 0 && (g.N / 96) * z % 256 == 0 && ((g.N + 63) / 64) * z % 256 != 0) {
-      if (g.M <= 64) MLA_SK(96, 64, g.N / 96);
-      else MLA_SK(96, 128, g.N / 96);
-      return;
-    }
-    if (g.M <= 64) MLA_SK(64, 64, (g.N + 63) / 64);
-    else MLA_SK(64, 128, (g.N + 63) / 64);
-#undef MLA_SK
+  if (!NN && skinny_ok(g)) {
+    if (g.xf32) launch_skinny<OUT, true>(g, skinny_prob(g), st);
+    else launch_skinny<OUT, false>(g, skinny_prob(g), st);
     return;
   }
+  if (g.xf32) return;                               // (callers check skinny_ok first)
   if (g.M <= 64)
     launch_bf16<64, 128, 64, NN, OUT>(g, st);
   else if (tiles_big >= 256)
@@ -803,14 +900,9 @@ bool launch_q_split_gemm(const GemmArgs& g, float* q_pe, hipStream_t st) {
   if (!skinny_ok(g) || g.nsplit != 1 || g.batch != 1 || g.N % 192 != 0) return false;
   SkinnyProb p = skinny_prob(g);
   p.Y2 = q_pe;
-  const bool w96 = g.N % 96 == 0 && (g.N / 96) % 256 == 0;
-  if (g.M <= 64) {
-    if (w96) hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 96, 64>), dim3(g.N / 96, 1, 1), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 64, 64>), dim3(g.N / 64, 1, 1), dim3(256), 0, st, p);
-  } else {
-    if (w96) hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 96, 128>), dim3(g.N / 96, 1, 1), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((gemm_skinny_kernel<kOutQSplit, 64, 128>), dim3(g.N / 64, 1, 1), dim3(256), 0, st, p);
-  }
+  const GemmArgs one = g;
+  if (g.xf32) launch_skinny<kOutQSplit, true>(one, p, st);
+  else launch_skinny<kOutQSplit, false>(one, p, st);
   return true;
 }
 
@@ -852,6 +944,7 @@ void launch_gemm(const GemmArgs& g, hipStream_t st) {
     return;
   }
   if (launch_gemm_tile(g, st)) return;
+  if (g.f16in || g.row_scale) return;               // (callers check launch_gemm_tile_ok first)
   if (g.nn) launch_bf16_out<true>(g, st);
   else launch_bf16_out<false>(g, st);
 }

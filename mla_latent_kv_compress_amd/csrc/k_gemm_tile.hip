@@ -1,5 +1,8 @@
-// Large-tile bf16 GEMM for the prefill projections (q_b and the kv_b decompression), TN with a
-// 2-byte output:  Y[z] = alpha * X[z] (M x K, row-major) * W[z]^T  (W [N][K], K contiguous).
+// Large-tile GEMM for the prefill projections (q_b and the kv_b decompression), TN with a
+// 2-byte output:  Y[z] = alpha * X[z] (M x K, row-major) * W[z]^T  (W [N][K], K contiguous),
+// operands bf16 or (F16IN) fp16; optionally each output row m of batch z is multiplied by
+// row_scale[z * srs + m] (fp32, before the output rounding: the fp8 cache's token scales).
+// fp16 outputs saturate at +-65504.
 //
 // One work-group of 8 waves per 256 x 256 output tile; wave w computes rows
 // [128 (w >> 2), +128) x columns [64 (w & 3), +64) as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
@@ -26,11 +29,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 }  // namespace
 
-template <int OUT>
+template <int OUT, bool F16IN>
 __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
     int M, int N, int K, int tiles_m, const uint16_t* __restrict__ X, long lda, long sx,
     const uint16_t* __restrict__ W, long ldw, long sw, uint16_t* __restrict__ Y, long ldc, long sy,
-    float alpha) {
+    float alpha, const float* __restrict__ row_scale, long srs) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,7 +99,13 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (F16IN)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a[i]),
+                                                               __builtin_bit_cast(f16x8_t, b[j]), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
     }
     lds::barrier();                                  // stage ks's buffer free for stage ks + 2
   }
@@ -104,6 +113,14 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
   // Result tile through LDS: [256][256] 2-byte values, 16-byte chunk c of row r at c ^ (r & 7).
   // C layout: lane holds C[8 (k >> 2) + 4 e + (k & 3)][lane & 31] of each 32 x 32 tile.
   uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
+  float rs[4][16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int m = 128 * wm + 32 * i + 8 * (k >> 2) + 4 * e + (k & 3);
+      rs[i][k] = row_scale ? alpha * row_scale[z * srs + min(m0 + m, M - 1)] : alpha;
+    }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -112,8 +129,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int m = 128 * wm + 32 * i + 8 * (k >> 2) + 4 * e + (k & 3);
-        const float v = alpha * acc[i][j][k];
-        ct[m * kTN + 8 * ((n >> 3) ^ (m & 7)) + (n & 7)] = OUT == S_BF16 ? f2bf(v) : f2h(v);
+        const float v = rs[i][k] * acc[i][j][k];
+        ct[m * kTN + 8 * ((n >> 3) ^ (m & 7)) + (n & 7)] = OUT == S_BF16 ? f2bf(v) : f2h_sat(v);
       }
     }
   lds::barrier();
@@ -127,9 +144,10 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
   }
 }
 
-bool launch_gemm_tile(const GemmArgs& g, hipStream_t st) {
-  if (g.kind != GEMM_BF16 || g.nn || g.nsplit != 1) return false;
+bool launch_gemm_tile_ok(const GemmArgs& g) {
+  if (g.kind != GEMM_BF16 || g.nn || g.nsplit != 1 || g.xf32) return false;
   if (g.out != K_BF16 && g.out != K_F16) return false;
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return false;
   if (g.K % kTK != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || g.ldw % 8 != 0 || g.ldc % 8 != 0) return false;
   if (g.sx % 8 != 0 || g.sw % 8 != 0 || g.sy % 8 != 0) return false;
   if ((reinterpret_cast<uintptr_t>(g.X) | reinterpret_cast<uintptr_t>(g.W) | reinterpret_cast<uintptr_t>(g.Y)) & 15)
@@ -137,16 +155,28 @@ bool launch_gemm_tile(const GemmArgs& g, hipStream_t st) {
   // 32-bit load offsets: 255 rows of X or W
   if (long(kTM) * g.lda * 2 >= (1L << 31) || long(kTN) * g.ldw * 2 >= (1L << 31)) return false;
   const long tiles_m = (g.M + kTM - 1) / kTM, tiles_n = (g.N + kTN - 1) / kTN;
-  if (tiles_m * tiles_n * g.batch < 256 || g.batch > 65535 || tiles_m * tiles_n > (1L << 30)) return false;
+  return g.batch <= 65535 && tiles_m * tiles_n <= (1L << 30);
+}
+
+bool launch_gemm_tile(const GemmArgs& g, hipStream_t st) {
+  if (!launch_gemm_tile_ok(g)) return false;
+  const long tiles_m = (g.M + kTM - 1) / kTM, tiles_n = (g.N + kTN - 1) / kTN;
+  // Plain products smaller than one round of work-groups go to the smaller-tile kernels; fp16
+  // operands and row scales exist only here.
+  if (!g.f16in && !g.row_scale && tiles_m * tiles_n * g.batch < 256) return false;
   const dim3 grid(unsigned(tiles_m * tiles_n), unsigned(g.batch));
-  if (g.out == K_BF16)
-    hipLaunchKernelGGL(gemm_tile_kernel<S_BF16>, grid, dim3(512), 0, st, g.M, g.N, g.K, int(tiles_m),
-                       static_cast<const uint16_t*>(g.X), g.lda, g.sx, static_cast<const uint16_t*>(g.W), g.ldw,
-                       g.sw, static_cast<uint16_t*>(g.Y), g.ldc, g.sy, g.alpha);
-  else
-    hipLaunchKernelGGL(gemm_tile_kernel<S_F16>, grid, dim3(512), 0, st, g.M, g.N, g.K, int(tiles_m),
-                       static_cast<const uint16_t*>(g.X), g.lda, g.sx, static_cast<const uint16_t*>(g.W), g.ldw,
-                       g.sw, static_cast<uint16_t*>(g.Y), g.ldc, g.sy, g.alpha);
+#define MLA_GT(OUT, F16)                                                                                       \
+  hipLaunchKernelGGL((gemm_tile_kernel<OUT, F16>), grid, dim3(512), 0, st, g.M, g.N, g.K, int(tiles_m),          \
+                     static_cast<const uint16_t*>(g.X), g.lda, g.sx, static_cast<const uint16_t*>(g.W), g.ldw,   \
+                     g.sw, static_cast<uint16_t*>(g.Y), g.ldc, g.sy, g.alpha, g.row_scale, g.srs)
+  if (g.out == K_BF16) {
+    if (g.f16in) MLA_GT(S_BF16, true);
+    else MLA_GT(S_BF16, false);
+  } else {
+    if (g.f16in) MLA_GT(S_F16, true);
+    else MLA_GT(S_F16, false);
+  }
+#undef MLA_GT
   return true;
 }
 

@@ -1,5 +1,7 @@
 // Row-wise kernels of the MLA path: cache-row epilogue of the KV compression, the query
 // RMSNorm and packing, index preparation, the split-K merge and the prefill gather.
+#include <algorithm>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -146,9 +148,9 @@ void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit,
 }
 
 // ------------------------------------------------------------------ RMSNorm of query latents
-template <typename ActT>
+template <typename ActT, typename OutT = ActT>
 __device__ __forceinline__ void rmsnorm_row(int t, int T, int n, int nsplit, const float* __restrict__ acc,
-                                            const ActT* __restrict__ gamma, ActT* __restrict__ out, float eps,
+                                            const ActT* __restrict__ gamma, OutT* __restrict__ out, float eps,
                                             float* row, float* red) {
   float ss = 0.f;
   if (n % 4 == 0) {
@@ -167,27 +169,28 @@ __device__ __forceinline__ void rmsnorm_row(int t, int T, int n, int nsplit, con
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / float(n) + eps);
   for (int i = threadIdx.x; i < n; i += blockDim.x)
-    stf<ActT>(out, long(t) * n + i, row[i] * r * ldf<ActT>(gamma, i));
+    stf<OutT>(out, long(t) * n + i, row[i] * r * ldf<ActT>(gamma, i));
 }
 
-template <typename ActT>
+template <typename ActT, typename OutT>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsplit,
                                                            const float* __restrict__ acc,
                                                            const ActT* __restrict__ gamma,
-                                                           ActT* __restrict__ out, float eps) {
+                                                           OutT* __restrict__ out, float eps) {
   extern __shared__ float row[];
   __shared__ float red[16];
-  rmsnorm_row<ActT>(blockIdx.x, T, n, nsplit, acc, gamma, out, eps, row, red);
+  rmsnorm_row<ActT, OutT>(blockIdx.x, T, n, nsplit, acc, gamma, out, eps, row, red);
 }
 
 // Decode: the compress epilogue of the T new tokens (blocks [0, T)) and the RMSNorm of their
-// query latents (blocks [T, 2T)) in one launch; the two read disjoint partials.
+// query latents (blocks [T, 2T), written in fp32: the query projection takes them as a bf16
+// hi + lo pair) in one launch; the two read disjoint partials.
 template <typename ActT, int CACHE>
 __global__ __launch_bounds__(256) void decode_rows_kernel(
     int dc, int dr, int T, int nsplit_kv, const float* __restrict__ acc_kv, const ActT* __restrict__ gamma_kv,
     void* __restrict__ cache, float* __restrict__ cache_scale, long num_slots, float eps, RopeParams rp,
     float* __restrict__ rope_tab, const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks,
-    int nq, int nsplit_q, const float* __restrict__ acc_q, const ActT* __restrict__ gamma_q, ActT* __restrict__ cq) {
+    int nq, int nsplit_q, const float* __restrict__ acc_q, const ActT* __restrict__ gamma_q, float* __restrict__ cq) {
   extern __shared__ float row[];                    // [max(dc + dr, nq)]
   __shared__ float red[16];
   const int t = blockIdx.x;
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(
     compress_row<ActT, CACHE>(t, dc, dr, T, nsplit_kv, acc_kv, gamma_kv, nullptr, nullptr, cache, cache_scale,
                               num_slots, eps, rp, rope_tab, ctx, bt, max_blocks, row, red);
   else
-    rmsnorm_row<ActT>(t - T, T, nq, nsplit_q, acc_q, gamma_q, cq, eps, row, red);
+    rmsnorm_row<ActT, float>(t - T, T, nq, nsplit_q, acc_q, gamma_q, cq, eps, row, red);
 }
 
 bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
@@ -208,7 +211,7 @@ bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv
   hipLaunchKernelGGL((decode_rows_kernel<uint16_t, C>), dim3(2 * T), dim3(256), sh, st, dc, dr, T, nsplit_kv, \
                      acc_kv, static_cast<const uint16_t*>(gamma_kv), cache_data, cache_scale, num_slots, eps, \
                      rp, rope_tab, ctx, bt, max_blocks, nq, nsplit_q, acc_q,                        \
-                     static_cast<const uint16_t*>(gamma_q), static_cast<uint16_t*>(cq))
+                     static_cast<const uint16_t*>(gamma_q), static_cast<float*>(cq))
   if (cache == K_BF16)
     MLA_DR(K_BF16);
   else
@@ -218,15 +221,40 @@ bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv
 }
 
 void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,
-                         void* out, float eps, hipStream_t st) {
+                         void* out, float eps, hipStream_t st, bool out_f16) {
   if (T <= 0) return;
   size_t sh = size_t(n) * sizeof(float);
   if (act == K_F32)
-    hipLaunchKernelGGL(rmsnorm_rows_kernel<float>, dim3(T), dim3(256), sh, st, T, n, nsplit, acc,
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<float, float>), dim3(T), dim3(256), sh, st, T, n, nsplit, acc,
                        static_cast<const float*>(gamma), static_cast<float*>(out), eps);
+  else if (out_f16)
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<uint16_t, F16Out>), dim3(T), dim3(256), sh, st, T, n, nsplit, acc,
+                       static_cast<const uint16_t*>(gamma), static_cast<F16Out*>(out), eps);
   else
-    hipLaunchKernelGGL(rmsnorm_rows_kernel<uint16_t>, dim3(T), dim3(256), sh, st, T, n, nsplit, acc,
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<uint16_t, uint16_t>), dim3(T), dim3(256), sh, st, T, n, nsplit, acc,
                        static_cast<const uint16_t*>(gamma), static_cast<uint16_t*>(out), eps);
+}
+
+// bf16 -> fp16 copy (saturating at +-65504; exact for magnitudes in [2^-14, 65504]).
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                          long n8) {
+  for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n8; i += long(gridDim.x) * 256) {
+    const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = uint32_t(f2h_sat(__uint_as_float(w[j] << 16))) | (uint32_t(f2h_sat(__uint_as_float(w[j] & 0xFFFF0000u))) << 16);
+    reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+void launch_bf16_to_f16(const void* src, void* dst, long n, hipStream_t st) {
+  if (n <= 0) return;
+  const long n8 = n / 8;
+  const long blocks = std::min<long>((n8 + 255) / 256, 8192);
+  hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                     static_cast<uint16_t*>(dst), n8);
 }
 
 // ------------------------------------------------------------------ query packing
@@ -485,14 +513,19 @@ void launch_decode_merge(int B, int H, int dc, int splits, const float* part_o, 
 }
 
 // ------------------------------------------------------------------ prefill gather
-// lat[s][t][:] = dequantised cache row of position t of sequence s, t < ctx_s; zero beyond.
+// lat[s][t][:] = cache row of position t of sequence s, t < ctx_s; zero beyond.  bf16 / fp32
+// caches: the stored values.  fp8 cache: the codes' values (exact in bf16), with the token's
+// scale in tscale[s][t] (1 beyond the context), which the decompression applies in fp32.  kpe16
+// (bf16 path) gets the k_pe part (columns [dc, W)) as fp16: the stored value, or scale * code
+// rounded once.
 template <typename ActT, int CACHE>
 __global__ __launch_bounds__(256) void gather_rows_kernel(int max_ctx, int W, int dc, const int32_t* __restrict__ cu,
                                                           const int32_t* __restrict__ start,
                                                           const int32_t* __restrict__ bt, int max_blocks,
                                                           const void* __restrict__ cache,
                                                           const float* __restrict__ cache_scale,
-                                                          ActT* __restrict__ lat, uint16_t* __restrict__ kpe16) {
+                                                          ActT* __restrict__ lat, uint16_t* __restrict__ kpe16,
+                                                          float* __restrict__ tscale) {
   const int s = blockIdx.y, t = blockIdx.x;
   const int ctx = start[s] + (cu[s + 1] - cu[s]);
   const long row = long(s) * max_ctx + t;
@@ -503,26 +536,29 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(int max_ctx, int W, in
       stf<ActT>(dst, i, 0.f);
       if (pe && i >= dc) pe[i - dc] = f2h(0.f);
     }
+    if (CACHE == K_FP8 && threadIdx.x == 0) tscale[row] = 1.f;
     return;
   }
   const long slot = long(bt[long(s) * max_blocks + t / kPage]) * kPage + t % kPage;
+  const float sc = CACHE == K_FP8 ? cache_scale[slot] : 1.f;
+  if (CACHE == K_FP8 && threadIdx.x == 0) tscale[row] = sc;
   for (int i = threadIdx.x; i < W; i += blockDim.x) {
     float v;
     if (CACHE == K_F32) v = static_cast<const float*>(cache)[slot * W + i];
     else if (CACHE == K_BF16) v = bf2f(static_cast<const uint16_t*>(cache)[slot * W + i]);
-    else v = cache_scale[slot] * e4m3_to_f(static_cast<const uint8_t*>(cache)[slot * W + i]);
+    else v = e4m3_to_f(static_cast<const uint8_t*>(cache)[slot * W + i]);
     stf<ActT>(dst, i, v);
-    if (pe && i >= dc) pe[i - dc] = f2h(v);
+    if (pe && i >= dc) pe[i - dc] = f2h_sat(sc * v);
   }
 }
 
 void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, int dc, const int32_t* cu,
                         const int32_t* start, const int32_t* bt, int max_blocks, const void* cache_data,
-                        const float* cache_scale, void* lat, void* kpe16, hipStream_t st) {
+                        const float* cache_scale, void* lat, void* kpe16, float* tscale, hipStream_t st) {
   dim3 grid(max_ctx, S);
 #define MLA_GR(A, C)                                                                                 \
   hipLaunchKernelGGL((gather_rows_kernel<A, C>), grid, dim3(256), 0, st, max_ctx, W, dc, cu, start, bt, \
-                     max_blocks, cache_data, cache_scale, static_cast<A*>(lat), static_cast<uint16_t*>(kpe16))
+                     max_blocks, cache_data, cache_scale, static_cast<A*>(lat), static_cast<uint16_t*>(kpe16), tscale)
   if (act == K_F32) {
     MLA_GR(float, K_F32);
   } else if (cache == K_BF16) {
@@ -531,6 +567,29 @@ void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, int dc, c
     MLA_GR(uint16_t, K_FP8);
   }
 #undef MLA_GR
+}
+
+// ------------------------------------------------------------------ fp8 codec
+__global__ __launch_bounds__(256) void fp8_encode_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
+                                                         long n) {
+  for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n; i += long(gridDim.x) * 256)
+    codes[i] = uint8_t(f_to_e4m3(x[i]));
+}
+__global__ __launch_bounds__(256) void fp8_decode_kernel(const uint8_t* __restrict__ codes, float* __restrict__ x,
+                                                         long n) {
+  for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n; i += long(gridDim.x) * 256)
+    x[i] = e4m3_to_f(codes[i]);
+}
+
+void launch_fp8_codec(bool encode, const void* in, void* out, long n, hipStream_t st) {
+  if (n <= 0) return;
+  const long blocks = std::min<long>((n + 255) / 256, 4096);
+  if (encode)
+    hipLaunchKernelGGL(fp8_encode_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, static_cast<const float*>(in),
+                       static_cast<uint8_t*>(out), n);
+  else
+    hipLaunchKernelGGL(fp8_decode_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, static_cast<const uint8_t*>(in),
+                       static_cast<float*>(out), n);
 }
 
 }  // namespace mla

@@ -52,43 +52,59 @@ void enqueue_compress(const Dims& d, Path path, const mla_config* cfg, const mla
 }
 
 // Query projection of T tokens.  Leaves fp32 partials at q.off_q_acc, or (q.direct) the scaled
-// fp16 queries in `direct_out` ([T][H][dqk]).
+// fp16 queries in `direct_out` ([T][H][dqk]).  With wq16 (a workspace region for an fp16 copy of
+// q_b_proj) the normed query latent is kept in fp16 and q_b runs on fp16 operands: the latent
+// carries 11 significant bits into the product instead of bf16's 8 (the copy is exact for
+// weights of magnitude 2^-14 .. 65504).
 void enqueue_query(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
                    const void* hidden, int T, const QueryPlan& q, void* ws, void* direct_out,
-                   float direct_scale, hipStream_t s) {
+                   float direct_scale, hipStream_t s, void* wq16 = nullptr) {
   const long nq = long(d.H) * d.dqk();
   void* qout = q.direct ? direct_out : at(ws, q.off_q_acc);
   const int out = q.direct ? K_F16 : K_F32;
   const float alpha = q.direct ? direct_scale : 1.f;
   const void* x = hidden;
+  const void* wb = w->q_b_proj;
   long ldx = d.D;
   if (d.dq > 0) {
     float* qa = reinterpret_cast<float*>(at(ws, q.off_qa_acc));
     void* cq = at(ws, q.off_cq);
     launch_gemm(gemm(path, false, K_F32, T, d.dq, d.D, q.split_a, 1, hidden, d.D, 0, w->q_a_proj, d.D, 0,
                      qa, d.dq, 0), s);
-    launch_rmsnorm_rows(kdt(cfg->act_dtype), T, d.dq, q.split_a.n, qa, w->q_a_norm, cq, d.eps, s);
+    launch_rmsnorm_rows(kdt(cfg->act_dtype), T, d.dq, q.split_a.n, qa, w->q_a_norm, cq, d.eps, s, wq16 != nullptr);
+    if (wq16) {
+      launch_bf16_to_f16(w->q_b_proj, wq16, nq * d.dq, s);
+      wb = wq16;
+    }
     x = cq;
     ldx = d.dq;
   }
-  launch_gemm(gemm(path, false, out, T, int(nq), int(ldx), q.split_b, 1, x, ldx, 0, w->q_b_proj, ldx, 0, qout,
-                   nq, 0, alpha), s);
+  GemmArgs g = gemm(path, false, out, T, int(nq), int(ldx), q.split_b, 1, x, ldx, 0, wb, ldx, 0, qout, nq, 0, alpha);
+  g.f16in = wq16 != nullptr;
+  launch_gemm(g, s);
 }
 
 // Decode front on the bf16 path with a query LoRA: the kv_a and q_a projections in one launch,
-// the compress epilogue and the query-latent RMSNorm in one launch, then q_b.  Same arithmetic
-// as enqueue_compress + enqueue_query; false (nothing enqueued) if the grouped launch does not
-// apply.
+// the compress epilogue and the query-latent RMSNorm in one launch, then q_b.  The normed query
+// latent stays fp32 and enters the q_b products as a bf16 hi + lo pair; with the split epilogue
+// (no K split, d_n 128, d_r 64) q_nope leaves scaled in fp32 for the absorb, q_pe in fp32.  Same
+// computation as enqueue_compress + enqueue_query up to rounding; false (nothing enqueued) if the
+// grouped launch does not apply.
 bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
                           const void* hidden, const mla_cache* cache, int B, const DecodePlan& p, void* ws,
                           float* rope, const int32_t* ctx, const int32_t* bt, int max_blocks, float qscale,
                           bool* qsplit, hipStream_t s) {
   *qsplit = false;
   const QueryPlan& q = p.q;
-  if (path != PATH_BF16 || d.dq <= 0 || q.direct) return false;
+  if (path != PATH_BF16 || d.dq <= 0 || q.direct || !p.cq_f32) return false;
   float* acc_kv = reinterpret_cast<float*>(at(ws, p.comp.off_acc));
   float* acc_q = reinterpret_cast<float*>(at(ws, q.off_qa_acc));
-  void* cq = at(ws, q.off_cq);
+  float* cq = reinterpret_cast<float*>(at(ws, q.off_cq));
+  const long nq = long(d.H) * d.dqk();
+  GemmArgs g_b = gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, d.dq, 0, w->q_b_proj, d.dq, 0,
+                      at(ws, q.off_q_acc), nq, 0);
+  g_b.xf32 = true;
+  if (!launch_gemm_skinny_ok(g_b)) return false;
   const GemmArgs g_q = gemm(path, false, K_F32, B, d.dq, d.D, q.split_a, 1, hidden, d.D, 0, w->q_a_proj, d.D, 0,
                             acc_q, d.dq, 0);
   const GemmArgs g_kv = gemm(path, false, K_F32, B, d.W(), d.D, p.comp.split, 1, hidden, d.D, 0, w->kv_a_proj,
@@ -97,33 +113,43 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
   const long num_slots = long(cache->num_blocks) * MLA_PAGE_SIZE;
   if (!launch_decode_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
                           w->kv_a_norm, cache->data, cache->scale, num_slots, d.eps, d.rope, rope, ctx, bt,
-                          max_blocks, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, s)) {
-    launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
-                         w->kv_a_norm, nullptr, nullptr, cache->data, cache->scale, num_slots, d.eps, d.rope, rope,
-                         ctx, bt, max_blocks, s);
-    launch_rmsnorm_rows(kdt(cfg->act_dtype), B, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, d.eps, s);
-  }
-  const long nq = long(d.H) * d.dqk();
-  // q_b with the split epilogue (q_nope as bf16(scale q), q_pe fp32, in the q_acc region) when
-  // it applies; the absorb kernel then reads half the bytes.
+                          max_blocks, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, s))
+    return false;                                 // (cannot happen: bf16 activations, bf16 / fp8 cache)
+  // q_b with the split epilogue (q_nope as fp32 scale q, q_pe fp32, in the q_acc region) when
+  // it applies.
   if (q.split_b.n == 1 && d.dn == 128 && d.dr == 64) {
     char* qn = at(ws, q.off_q_acc);
-    float* qpe = reinterpret_cast<float*>(qn + size_t(B) * d.H * d.dn * 2);
-    if (launch_q_split_gemm(gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, d.dq, 0, w->q_b_proj, d.dq,
-                                 0, qn, nq, 0, qscale),
-                            qpe, s)) {
+    float* qpe = reinterpret_cast<float*>(qn + size_t(B) * d.H * d.dn * 4);
+    GemmArgs g = g_b;
+    g.alpha = qscale;
+    if (launch_q_split_gemm(g, qpe, s)) {
       *qsplit = true;
       return true;
     }
   }
-  launch_gemm(gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, d.dq, 0, w->q_b_proj, d.dq, 0,
-                   at(ws, q.off_q_acc), nq, 0), s);
+  launch_gemm(g_b, s);
   return true;
 }
 
 }  // namespace
 
 extern "C" {
+
+int mla_fp8_e4m3_encode(const float* x, uint8_t* codes, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!x || !codes))) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  (void)hipGetLastError();
+  launch_fp8_codec(true, x, codes, long(n), static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+int mla_fp8_e4m3_decode(const uint8_t* codes, float* x, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!x || !codes))) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  (void)hipGetLastError();
+  launch_fp8_codec(false, codes, x, long(n), static_cast<hipStream_t>(stream));
+  return finish();
+}
 
 const char* mla_status_string(int status) {
   switch (status) {
@@ -229,11 +255,11 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   const float* qacc = reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc));
   // Absorb: qhat[b][h][0:dc] = q_nope[b][h] . W_UK^h  (W_UK^h = kv_b_proj rows of head h's k_nope),
   // qhat[b][h][dc:] = RoPE(q_pe[b][h]); one kernel on the bf16 path.
-  const void* qn16 = qsplit ? at(workspace, p.q.off_q_acc) : nullptr;
-  const float* qpe32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc) + size_t(B) * d.H * d.dn * 2)
+  const float* qn32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)) : nullptr;
+  const float* qpe32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc) + size_t(B) * d.H * d.dn * 4)
                               : nullptr;
   if (!(path == PATH_BF16 && launch_absorb_rope(B, d.H, d.dn, d.dr, d.dc, d.dv, p.q.split_b.n, qacc, rope, qscale,
-                                                w->kv_b_proj, qhat, s, qn16, qpe32))) {
+                                                w->kv_b_proj, qhat, s, qn32, qpe32))) {
     if (qsplit) return MLA_ERR_UNSUPPORTED;       // (cannot happen: both need dn 128, dr 64, dc 512)
     if (path == PATH_BF16) launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
     launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n, qacc, pos, qscale, d.rope, qnope, qhat,
@@ -306,6 +332,14 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
   PrefillPlan p;
   plan_prefill(d, path, num_seqs, total_tokens, max_q_len, max_ctx, &p);
   if (!workspace || workspace_bytes < p.bytes) return MLA_ERR_WORKSPACE;
+  if (path == PATH_BF16 && cfg->cache_dtype == MLA_FP8_E4M3) {
+    // the fp8 decompression applies the token scales in the large-tile kernel's epilogue
+    GemmArgs probe = gemm(path, false, K_F16, max_ctx, int(long(d.H) * d.dkv()), d.dc, whole(d.dc), num_seqs,
+                          at(workspace, p.off_lat), d.W(), long(max_ctx) * d.W(), w->kv_b_proj, d.dc, 0,
+                          at(workspace, p.off_kv), long(d.H) * d.dkv(), long(max_ctx) * d.H * d.dkv());
+    probe.row_scale = reinterpret_cast<const float*>(at(workspace, p.off_tscale));
+    if (!launch_gemm_tile_ok(probe)) return MLA_ERR_UNSUPPORTED;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const int act = kdt(cfg->act_dtype);
@@ -319,7 +353,14 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
   void* qs = at(workspace, p.off_qs);
   const float qscale = d.sigma * kLog2eHost;
   const int qs_type = path == PATH_F32 ? K_F32 : K_F16;
-  enqueue_query(d, path, cfg, w, hidden, T, p.q, workspace, qs, qscale, s);
+  void* wq16 = nullptr;
+  if (p.q16) {
+    GemmArgs probe = gemm(path, false, K_F16, T, int(long(d.H) * d.dqk()), d.dq, p.q.split_b, 1, at(workspace, p.q.off_cq),
+                          d.dq, 0, at(workspace, p.off_wq16), d.dq, 0, qs, long(d.H) * d.dqk(), 0);
+    probe.f16in = true;
+    if (launch_gemm_tile_ok(probe)) wq16 = at(workspace, p.off_wq16);
+  }
+  enqueue_query(d, path, cfg, w, hidden, T, p.q, workspace, qs, qscale, s, wq16);
   if (p.q.direct)
     launch_q_rope_f16(T, d.H, d.dn, d.dr, pos, d.rope, qs, s);
   else
@@ -328,13 +369,21 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
                   nullptr, qs, s);
   void* lat = at(workspace, p.off_lat);
   void* kpe = path == PATH_BF16 ? at(workspace, p.off_kpe) : nullptr;
+  const bool fp8 = path == PATH_BF16 && cfg->cache_dtype == MLA_FP8_E4M3;
+  float* tscale = fp8 ? reinterpret_cast<float*>(at(workspace, p.off_tscale)) : nullptr;
   launch_gather_rows(act, kdt(cfg->cache_dtype), S, max_ctx, d.W(), d.dc, cu_seqlens, start_pos, block_table,
-                     max_blocks, cache->data, cache->scale, lat, kpe, s);
-  // Decompress every context latent: kv[s][t] = kv_b_proj . latent -> per head [k_nope | v].
+                     max_blocks, cache->data, cache->scale, lat, kpe, tscale, s);
+  // Decompress every context latent: kv[s][t] = kv_b_proj . latent -> per head [k_nope | v]
+  // (fp8 cache: kv_b_proj . codes, times the token's scale in fp32).
   void* kv = at(workspace, p.off_kv);
   const long nkv = long(d.H) * d.dkv();
-  launch_gemm(gemm(path, false, K_F16, max_ctx, int(nkv), d.dc, whole(d.dc), S, lat, d.W(),
-                   long(max_ctx) * d.W(), w->kv_b_proj, d.dc, 0, kv, nkv, long(max_ctx) * nkv), s);
+  GemmArgs gkv = gemm(path, false, K_F16, max_ctx, int(nkv), d.dc, whole(d.dc), S, lat, d.W(), long(max_ctx) * d.W(),
+                      w->kv_b_proj, d.dc, 0, kv, nkv, long(max_ctx) * nkv);
+  if (fp8) {
+    gkv.row_scale = tscale;
+    gkv.srs = max_ctx;
+  }
+  launch_gemm(gkv, s);
   PrefillAttnArgs a;
   a.S = S; a.H = d.H; a.dn = d.dn; a.dr = d.dr; a.dv = d.dv; a.dc = d.dc;
   a.max_q = max_q_len; a.max_ctx = max_ctx; a.out_type = kdt(cfg->out_dtype);

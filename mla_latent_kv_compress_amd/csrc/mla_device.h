@@ -27,16 +27,19 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // OCP e4m3fn ("fn": no infinities; 0x7F/0xFF are NaN; largest finite 448).
 __device__ __forceinline__ float e4m3_to_f(uint32_t c) {
   uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if ((c & 0x7Fu) == 0x7Fu) return __uint_as_float(0x7FC00000u);
   float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;
   return (c & 0x80u) ? -v : v;
 }
-// Nearest e4m3fn code of v (ties to even), saturating at +-448.
+// Nearest e4m3fn code of v (ties to even), saturating at +-448; NaN gives the NaN code.
 __device__ __forceinline__ uint32_t f_to_e4m3(float v) {
   uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
   float a = fabsf(v);
   uint32_t code;
-  if (!(a < 448.0f)) {
-    code = 0x7Eu;                                   // 448 (also for NaN input, never produced)
+  if (a != a) {
+    code = 0x7Fu;
+  } else if (!(a < 448.0f)) {
+    code = 0x7Eu;                                   // 448
   } else if (a < 0.015625f) {                       // below 2^-6: subnormal step 2^-9
     code = uint32_t(rintf(a * 512.0f));             // 8 carries into the smallest normal
   } else {
@@ -53,6 +56,8 @@ __device__ __forceinline__ uint32_t f_to_e4m3(float v) {
 // fp16 storage is uint16_t bit patterns as well (IEEE binary16, round to nearest even).
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 __device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
+// The same, saturating at +-65504 instead of overflowing to infinity.
+__device__ __forceinline__ uint16_t f2h_sat(float f) { return f2h(fminf(fmaxf(f, -65504.0f), 65504.0f)); }
 
 // Storage codes: fp32, bf16, fp16 (the fp8 cache has its own path).
 enum { S_F32 = 0, S_BF16 = 1, S_F16 = 3 };
@@ -67,12 +72,16 @@ template <> __device__ __forceinline__ void sts_<S_F32>(float* p, long i, float 
 template <> __device__ __forceinline__ void sts_<S_BF16>(uint16_t* p, long i, float v) { p[i] = f2bf(v); }
 template <> __device__ __forceinline__ void sts_<S_F16>(uint16_t* p, long i, float v) { p[i] = f2h(v); }
 
+// fp16 storage in the typed helpers below (a distinct type from bf16's uint16_t).
+struct F16Out { uint16_t bits; };
+
 template <typename T> __device__ __forceinline__ float ldf(const T* p, long i);
 template <> __device__ __forceinline__ float ldf<float>(const float* p, long i) { return p[i]; }
 template <> __device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p, long i) { return bf2f(p[i]); }
 template <typename T> __device__ __forceinline__ void stf(T* p, long i, float v);
 template <> __device__ __forceinline__ void stf<float>(float* p, long i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void stf<uint16_t>(uint16_t* p, long i, float v) { p[i] = f2bf(v); }
+template <> __device__ __forceinline__ void stf<F16Out>(F16Out* p, long i, float v) { p[i].bits = f2h_sat(v); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -21,11 +21,22 @@ struct GemmArgs {
   const void* W; long ldw, sw;
   void* Y; long ldc, sy, ssplit;
   float alpha;
+  bool xf32 = false;         // X is fp32 and enters the bf16 products as a hi + lo pair (skinny
+                             // kernel only: launch_gemm_skinny_ok must hold)
+  bool f16in = false;        // X and W are fp16 (large-tile kernel only)
+  const float* row_scale = nullptr;  // large-tile kernel: output row m of batch z times
+  long srs = 0;                      // row_scale[z * srs + m]
 };
 void launch_gemm(const GemmArgs& g, hipStream_t st);
 // 256 x 256-tile GEMM (k_gemm_tile.hip) for large TN products with a bf16 or fp16 output and no K
-// split (the prefill's q_b projection and kv_b decompression); false if the problem does not fit.
+// split (the prefill's q_b projection and kv_b decompression), bf16 or fp16 operands, optional
+// per-row output scale; false if the problem does not fit.
 bool launch_gemm_tile(const GemmArgs& g, hipStream_t st);
+// Whether the large-tile kernel takes the problem's shape (always so for fp16 operands or a row
+// scale, which only it implements).
+bool launch_gemm_tile_ok(const GemmArgs& g);
+// Whether the skinny (decode-batch) kernel takes this problem; required for xf32.
+bool launch_gemm_skinny_ok(const GemmArgs& g);
 // Two independent fp32-output skinny GEMMs in one launch; false (nothing launched) when either
 // does not meet the skinny kernel's conditions.
 bool launch_gemm_pair(const GemmArgs& a, const GemmArgs& b, hipStream_t st);
@@ -40,21 +51,27 @@ void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit,
                           const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
                           hipStream_t st);
 // Decode queries on the bf16 path, from the fp32 query projection q ([nsplit][B][H][dn + dr]):
-// qhat[b][h] = [ W_UK^h^T bf16(scale q_nope) | bf16(scale RoPE(q_pe)) ] (bf16), with the
-// angles of each token from rope_tab ([B][dr]: cos | sin).  False if the shape does not apply.
+// qhat[b][h] = [ W_UK^h^T (scale q_nope) (bf16, dc values) | scale RoPE(q_pe) (fp16, dr values) ],
+// q_nope entering the products as a bf16 hi + lo pair; the angles of each token come from
+// rope_tab ([B][dr]: cos | sin).  With q_nope32 / q_pe32 the query comes from the split epilogue
+// instead (q_nope32 already scaled).  False if the shape does not apply (dn 128, dc 512).
 bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit, const float* q_acc,
                         const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st,
-                        const void* q_nope16 = nullptr, const float* q_pe32 = nullptr);
-// Decode q_b projection (no K split, N = H x 192) whose epilogue stores q_nope as bf16(alpha q)
-// to g.Y [M][H][128] and q_pe as fp32 to q_pe [M][H][64] (the absorb kernel's QS input); false
-// (nothing launched) if the skinny kernel does not apply.
+                        const float* q_nope32 = nullptr, const float* q_pe32 = nullptr);
+// Decode q_b projection (no K split, N = H x 192) whose epilogue stores q_nope as fp32 alpha q
+// to g.Y [M][H][128] and q_pe as fp32 q to q_pe [M][H][64] (the absorb kernel's split input);
+// false (nothing launched) if the skinny kernel does not apply.
 bool launch_q_split_gemm(const GemmArgs& g, float* q_pe, hipStream_t st);
 
-// out[t][:] = RMSNorm(sum_s acc[s][t][:]) * gamma, in act dtype.
+// out[t][:] = RMSNorm(sum_s acc[s][t][:]) * gamma, in act dtype (or fp16, saturating, with
+// out_f16 on the bf16 path).
 void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, const void* gamma,
-                         void* out, float eps, hipStream_t st);
+                         void* out, float eps, hipStream_t st, bool out_f16 = false);
+// dst = fp16 copy of n bf16 values (n a multiple of 8, 16-byte aligned), saturating at +-65504.
+void launch_bf16_to_f16(const void* src, void* dst, long n, hipStream_t st);
 // Decode, bf16 activations: the compress epilogue (positions from the context lengths, RoPE
-// table written) and the query-latent RMSNorm in one launch of 2T blocks; false if unsupported.
+// table written) and the query-latent RMSNorm (cq: fp32 [T][nq]) in one launch of 2T blocks;
+// false if unsupported.
 bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
                         const void* gamma_kv, void* cache_data, float* cache_scale, long num_slots, float eps,
                         const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
@@ -109,12 +126,13 @@ void launch_merge_splits(int B, int H, int dc, int splits, const uint16_t* part_
 void launch_decode_merge(int B, int H, int dc, int splits, const float* part_o, const float* part_ml,
                          float* otilde, hipStream_t st);
 
-// Prefill: gather (and dequantise) each sequence's cached rows [0, ctx) into lat [S][max_ctx][W];
-// with kpe16 also their k_pe part (columns [dc, W)) in fp16 into kpe16 [S][max_ctx][W - dc].
+// Prefill: gather each sequence's cached rows [0, ctx) into lat [S][max_ctx][W] (an fp8 cache's
+// codes as their exact values, the token scales into tscale [S][max_ctx]); with kpe16 also their
+// k_pe part (columns [dc, W), dequantised) in fp16 into kpe16 [S][max_ctx][W - dc].
 void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, int dc, const int32_t* cu,
                         const int32_t* start, const int32_t* bt, int max_blocks,
                         const void* cache_data, const float* cache_scale, void* lat, void* kpe16,
-                        hipStream_t st);
+                        float* tscale, hipStream_t st);
 
 // Causal attention of packed chunk queries against decompressed keys / values.
 struct PrefillAttnArgs {
@@ -130,5 +148,8 @@ void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st);
 // Flash-style causal prefill attention (k_prefill.hip), bf16 path with nope 128, rope 64, v 128,
 // d_c 512; false if the shape does not apply.
 bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st);
+
+// Elementwise e4m3fn codec of the fp8 cache: encode fp32 -> codes, or decode codes -> fp32.
+void launch_fp8_codec(bool encode, const void* in, void* out, long n, hipStream_t st);
 
 }  // namespace mla

@@ -113,7 +113,7 @@ static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q
   if (d.dq > 0) {
     q->split_a = force_a ? *force_a : gemm_splitk(T, d.dq, d.D, 64, 64);
     q->off_qa_acc = L.take(size_t(q->split_a.n) * T * d.dq * 4);
-    q->off_cq = L.take(size_t(T) * d.dq * (path == PATH_F32 ? 4 : 2));
+    q->off_cq = L.take(size_t(T) * d.dq * 4);
     q->split_b = gemm_splitk(T, nq, d.dq, 64, 64);
   } else {
     q->split_a = SplitK{1, 32};
@@ -154,6 +154,7 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   const SplitK* force = pair.n > 0 ? &pair : nullptr;
   plan_compress(d, path, B, L, &p->comp, force);
   plan_query(d, path, B, L, &p->q, false, force);
+  p->cq_f32 = path == PATH_BF16 && d.dq > 0 && d.dq % 64 == 0;
   p->off_pos = L.take(size_t(B) * 4);
   p->off_slot = L.take(size_t(B) * 8);
   p->off_qnope = L.take(size_t(B) * d.H * d.dn * act);
@@ -183,6 +184,9 @@ int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx,
   p->off_lat = L.take(size_t(S) * max_ctx * d.W() * act);
   p->off_kpe = L.take(size_t(S) * max_ctx * d.dr * 2);
   p->off_kv = L.take(size_t(S) * max_ctx * d.H * d.dkv() * act);
+  p->off_tscale = L.take(path == PATH_BF16 && d.cache_dt == MLA_FP8_E4M3 ? size_t(S) * max_ctx * 4 : 0);
+  p->q16 = path == PATH_BF16 && d.dq > 0 && d.dq % 64 == 0 && p->q.direct;
+  p->off_wq16 = L.take(p->q16 ? size_t(d.H) * d.dqk() * d.dq * 2 : 0);
   p->bytes = L.top;
   return MLA_OK;
 }

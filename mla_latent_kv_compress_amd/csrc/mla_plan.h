@@ -61,7 +61,8 @@ struct QueryPlan {            // q path for T tokens, shared by decode and prefi
   bool direct;                // prefill, bf16 path, no K split: the q projection writes the
                               // scaled fp16 queries straight into their final buffer
   size_t off_qa_acc;          // fp32 [split_a.n][T][dq]          (dq > 0)
-  size_t off_cq;              // act  [T][dq]                      (dq > 0)
+  size_t off_cq;              // [T][dq] normed query latent       (dq > 0): act dtype, or fp32
+                              // (decode, bf16 path) -- room for fp32 either way on the bf16 path
   size_t off_q_acc;           // fp32 [split_b.n][T][H*dqk]        (!direct)
 };
 
@@ -75,6 +76,8 @@ constexpr int kOrderMax = 2048;
 
 struct DecodePlan {
   int splits;
+  bool cq_f32;                // the grouped decode front applies: fp32 query latent, taken by the
+                              // q_b projection as a bf16 hi + lo pair (bf16 path, dq > 0, dq % 64 == 0)
   bool ordered;               // rank the sequences by length before the attention (more than one
                               // round of work-groups on the 64-head kernel, at most 8 splits)
   size_t off_order;           // int32 [B]
@@ -103,6 +106,10 @@ struct PrefillPlan {
   size_t off_lat;             // act  [S][max_ctx][W] gathered (dequantised) cache rows
   size_t off_kpe;             // fp16 [S][max_ctx][dr] their k_pe part (bf16 path)
   size_t off_kv;              // [S][max_ctx][H*dkv] decompressed k_nope | v (fp32; fp16 on the bf16 path)
+  size_t off_tscale;          // fp32 [S][max_ctx] token scales of an fp8 cache (bf16 path)
+  size_t off_wq16;            // fp16 copy of q_b_proj (bf16 path with a query LoRA, q16)
+  bool q16;                   // bf16 path, dq > 0, dq % 64 == 0: the normed query latent and
+                              // q_b_proj enter the q_b projection in fp16
   size_t bytes;
 };
 int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, PrefillPlan* p);

@@ -52,12 +52,21 @@ def token_err(got, ref):
     return max(rel_err(got[i], ref[i]) for i in range(len(ref)))
 
 
+def bf16_half_quantum(x):
+    """Half the spacing of bfloat16 values around each x: the most a round-to-nearest store of x
+    in bf16 can move it (x = m 2^e with 0.5 <= |m| < 1 has quantum 2^(e - 8))."""
+    _, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(1.0, np.maximum(e - 9, -134))
+
+
 def bf16_out_ok(got, ref, bar):
-    """A bf16 output may add its own rounding (half an ulp, <= 2^-8 of the value) to the bar."""
+    """A bf16 output within the bar, plus the format's own rounding of each value: |got - ref| <=
+    bar * rms(ref) + half a bf16 quantum of ref (the store of an exact result could move it that
+    far; the computation's error is what the bar bounds)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     rms = np.sqrt(np.mean(ref * ref))
-    return bool(np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + bar * rms))
+    return bool(np.all(np.abs(got - ref) <= bar * rms + bf16_half_quantum(ref)))
 
 
 # Error bars: max|err| / rms(out) per output token, fp32 output.
