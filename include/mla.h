@@ -19,7 +19,8 @@
  * Conventions for every entry point
  *   - All data pointers are device memory owned by the caller, contiguous, row-major, in the
  *     layouts stated below.  The library allocates nothing, keeps no pointer after a call
- *     returns, holds no global state (calls are thread-safe) and never synchronises.
+ *     returns, holds no global state (calls are thread-safe) and never synchronises; the one
+ *     exception is mla_decode_noalloc's static per-GPU workspace (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
  *     asynchronously; the caller orders later reads after it on that stream.
  *   - Every argument is validated on the host before anything is enqueued.  On an error
@@ -174,6 +175,25 @@ int mla_decode_timed(const mla_config *cfg, const mla_weights *w, const void *hi
                      const mla_cache *cache, int32_t batch, int32_t num_splits, void *workspace,
                      size_t workspace_bytes, void *out, void *stream, void *ev_attn_begin,
                      void *ev_attn_end);
+
+/* ---------------------------------------------------------------------------------------
+ * mla_decode_noalloc: mla_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments
+ * and results as mla_decode without the workspace: the library uses a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB), one copy on each GPU it runs on, held until the process
+ * ends; it allocates nothing and calls no allocating routine.  Returns MLA_ERR_WORKSPACE when
+ * mla_decode_workspace_size(cfg, batch, max_blocks, num_splits) exceeds the array (e.g. a
+ * 236B-shaped batch of 64 x 8192 tokens with 2 splits needs 57.4 MB and fits; 128 sequences
+ * do not).  All calls on one GPU share its array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe.  The device address of the array is looked
+ * up once per GPU on the first call (MLA_ERR_HIP if that fails).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const void *hidden,
+                       const int32_t *context_lens, const int32_t *block_table, int32_t max_blocks,
+                       const mla_cache *cache, int32_t batch, int32_t num_splits, void *out,
+                       void *stream);
 
 /* ---------------------------------------------------------------------------------------
  * mla_prefill: causal prefill of one chunk per sequence, explicit (decompressing) form.

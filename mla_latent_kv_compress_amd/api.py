@@ -60,6 +60,8 @@ SIGNATURES = {
                                         _i32, _vp, _sz, _vp, _vp, _vp, _vp]),
     "mla_fp8_e4m3_encode": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
     "mla_fp8_e4m3_decode": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
+    "mla_decode_noalloc": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
+                                          _i32, _vp, _vp]),
     "mla_prefill_workspace_size": (_sz, [_P(MlaConfig), _i32, _i32, _i32, _i32]),
     "mla_prefill": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                    _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
@@ -194,6 +196,20 @@ def decode(cfg, weights, hidden, context_lens, block_table, cache, num_splits=0,
                                   _ptr(block_table), max_blocks, ctypes.byref(cs), B, num_splits, _ptr(ws), nbytes,
                                   _ptr(out), _stream(stream), ctypes.c_void_p(attn_events[0]),
                                   ctypes.c_void_p(attn_events[1])), "mla_decode_timed")
+    return out
+
+
+def decode_noalloc(cfg, weights, hidden, context_lens, block_table, cache, num_splits=0, out=None, stream=None):
+    """mla_decode_noalloc: the decode step on the library's static per-GPU workspace."""
+    L = lib()
+    B, max_blocks = block_table.shape
+    if out is None:
+        out = torch.empty((B, cfg.num_heads, cfg.v_head_dim), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
+    W = make_weights(weights)
+    cs = cache.struct()
+    _check(L.mla_decode_noalloc(ctypes.byref(cfg), ctypes.byref(W), _ptr(hidden), _ptr(context_lens),
+                                _ptr(block_table), max_blocks, ctypes.byref(cs), B, num_splits, _ptr(out),
+                                _stream(stream)), "mla_decode_noalloc")
     return out
 
 

@@ -1,13 +1,44 @@
 // extern "C" entry points of libmla: validate on the host, then enqueue the kernel pipeline.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "mla.h"
 #include "mla_kernels.h"
 #include "mla_plan.h"
 
 using namespace mla;
 
+// Workspace of mla_decode_noalloc: a file-scope device array, one copy on each GPU the library
+// runs on, held until the process ends.  Host code never uses its name as an address: the
+// device address comes from hipGetSymbolAddress, once per device (scratch_base below).
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_base[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (looked up on first use).
+int scratch_base(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MLA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_base[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MLA_ERR_HIP;
+    }
+    g_scratch_base[dev] = p;
+  }
+  *out = g_scratch_base[dev];
+  return MLA_OK;
+}
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
@@ -304,6 +335,27 @@ int mla_decode(const mla_config* cfg, const mla_weights* w, const void* hidden,
                size_t workspace_bytes, void* out, void* stream) {
   return mla_decode_timed(cfg, w, hidden, context_lens, block_table, max_blocks, cache, batch, num_splits,
                           workspace, workspace_bytes, out, stream, nullptr, nullptr);
+}
+
+int mla_decode_noalloc(const mla_config* cfg, const mla_weights* w, const void* hidden,
+                       const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks,
+                       const mla_cache* cache, int32_t batch, int32_t num_splits, void* out, void* stream) {
+  int st = check_decode_args(cfg, w, hidden, context_lens, block_table, max_blocks, cache, batch,
+                             num_splits, out);
+  if (st != MLA_OK) return st;
+  Dims d;
+  Path path;
+  check_config(cfg, &d, &path);
+  DecodePlan p;
+  plan_decode(d, path, batch, max_blocks, num_splits, &p);
+  if (p.bytes > size_t(MLA_NOALLOC_SCRATCH_BYTES)) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_base(&ws);
+  if (st != MLA_OK) return st;
+  // Every region of the plan is written before it is read within the call (split partials,
+  // states, queries), so nothing needs clearing between calls.
+  return mla_decode(cfg, w, hidden, context_lens, block_table, max_blocks, cache, batch, num_splits, ws,
+                    size_t(MLA_NOALLOC_SCRATCH_BYTES), out, stream);
 }
 
 size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_seqs, int32_t total_tokens,

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     L = api.lib()
     for n in names:
         assert hasattr(L, n), n
