@@ -20,13 +20,13 @@ values themselves are pinned only through those checks (see the design notes, "p
 unpinned").
 """
 from .mla import (Dims, rms_norm, rope, rope_frequencies, kv_rows, cache_rows, queries, head_weights, softmax,
-                  attend_explicit, attend_absorbed, decode_one, prefill_chunk)
+                  attend_explicit, attend_absorbed, decode_one, prefill_chunk, output_projection)
 from .numerics import (E4M3_MAX, fp32_round, bf16_round, e4m3_quantise, e4m3_encode_values,
                        e4m3_decode_codes, fp8_store, store_rows)
 
 __all__ = [
     "Dims", "rms_norm", "rope", "rope_frequencies", "kv_rows", "cache_rows", "queries", "head_weights", "softmax",
-    "attend_explicit", "attend_absorbed", "decode_one", "prefill_chunk",
+    "attend_explicit", "attend_absorbed", "decode_one", "prefill_chunk", "output_projection",
     "E4M3_MAX", "fp32_round", "bf16_round", "e4m3_quantise", "e4m3_encode_values",
     "e4m3_decode_codes", "fp8_store", "store_rows",
 ]

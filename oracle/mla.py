@@ -252,3 +252,17 @@ def prefill_chunk(dims, W, x, start_pos, prior_rows, cache_dtype, heads=None, qu
     q_nope, q_pe = queries(dims, W, x[sel], pos[sel])
     out = attend_explicit(dims, W, q_nope, q_pe, rows, heads=heads, causal_limit=pos[sel] + 1)
     return out, new_rows
+
+
+def output_projection(dims, W, o):
+    """The attention output taken back to the model width: the last step of the forward flow.
+
+    [MTRT], section "MLA 的两个核心部件": the flow ends with the attention result passed on as
+    the layer's output.  The pages name no output projection; the reading taken is a linear
+    layer o_proj of (out, in) layout [hidden, H * d_v] applied to the heads' outputs laid side by
+    side in head order (head h fills inputs h * d_v .. h * d_v + d_v - 1), as the input
+    projections are laid out.  o: [..., H, d_v]  ->  [..., hidden].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    flat = o.reshape(o.shape[:-2] + (dims.heads * dims.v_head,))
+    return flat @ np.asarray(W["o_proj"], dtype=np.float64).T

@@ -247,6 +247,37 @@ def test_peaked_scores_select_the_matching_key():
     np.testing.assert_allclose(out2[0, 0], rows[1, 4:8], atol=1e-6)
 
 
+# ---------------------------------------------------------------- output projection (o_proj reading)
+def test_output_projection_selects_head_major_inputs():
+    """A 0/1 o_proj that picks input j_i for output i returns head j_i // d_v's entry j_i % d_v
+    (heads side by side in head order): a transposed weight, or heads interleaved feature-major,
+    picks other entries (the selection is not an involution and rows differ from columns)."""
+    d = Dims(10, 3, 0, 8, 4, 4, 4)                      # H * d_v = 12 inputs, 10 outputs
+    o = np.array([[[100 * h + j + 0.5 for j in range(d.v_head)] for h in range(d.heads)]], dtype=np.float64)
+    pick = np.random.default_rng(31).permutation(d.heads * d.v_head)[: d.hidden]
+    w = np.zeros((d.hidden, d.heads * d.v_head))
+    w[np.arange(d.hidden), pick] = 1.0
+    out = oracle.output_projection(d, {"o_proj": w}, o)
+    assert out.shape == (1, d.hidden)
+    np.testing.assert_array_equal(out[0], [100 * (j // d.v_head) + j % d.v_head + 0.5 for j in pick])
+
+
+def test_output_projection_brute_force():
+    """Against a scalar triple loop (output i = sum over heads h and features j of
+    o_proj[i][h d_v + j] o[h][j]) on a small random case, two tokens at once."""
+    d = Dims(6, 3, 0, 8, 4, 4, 5)
+    g = np.random.default_rng(32)
+    o = g.standard_normal((2, d.heads, d.v_head))
+    w = g.standard_normal((d.hidden, d.heads * d.v_head))
+    want = np.zeros((2, d.hidden))
+    for t in range(2):
+        for i in range(d.hidden):
+            for h in range(d.heads):
+                for j in range(d.v_head):
+                    want[t, i] += w[i, h * d.v_head + j] * o[t, h, j]
+    np.testing.assert_allclose(oracle.output_projection(d, {"o_proj": w}, o), want, rtol=1e-13, atol=1e-13)
+
+
 # ---------------------------------------------------------------- P10 / P11: causality and chunking
 def test_p10_causality():
     d = SHAPES["tiny"]
