@@ -4,17 +4,23 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-detail]
 
 A step is one mla_decode call: compress and append each new token, the query path with the
-k_nope absorption, split-K attention over the paged latent cache, the log-sum-exp merge and the
-v projection.  Inputs are seeded synthetic data already resident in HBM.
+k_nope absorption, split-K attention over the paged latent cache, the log-sum-exp merge, the
+v projection and the output projection o_proj (the layer's whole attention step).  Inputs are
+seeded synthetic data already resident in HBM.
 
 Timing protocol: W untimed warm-up steps; then K steps, each preceded (outside its timed region)
-by a 512 MiB write to a scratch buffer that evicts the caches (the 256 MB Infinity Cache would
-otherwise hold the weights, and all of a small workload's cache, between steps); each step is
+by a read of a 1 GiB buffer through the library's stream-read reference kernel, which evicts the
+caches (the 256 MB Infinity Cache would otherwise hold the weights, and all of a small
+workload's cache, between steps) and leaves only clean lines behind: a write-based flush leaves
+up to 256 MB of dirty lines whose write-back then runs inside the next timed step (measured: a
+plain 604 MB read took 172 us after a 512 MiB fill, 119 us after the read sweep).  Each step is
 bracketed by HIP events on the library's stream, and the line reports the median with p10 / p90.
 A second pass over the same K flushed steps records HIP events around the attention kernel
 alone (an event recorded inside the step costs a few microseconds of its own, so the two are
 separate passes); the dominant kernel's roofline uses that kernel's mean duration.  A third pass
-times K steps back to back between two synchronisations (caches warm), reported beside it.
+times K steps back to back between two synchronisations (caches warm), reported beside it; a
+fourth captures the step once in a HIP graph and replays it K times under the same flush (the
+gaps between the step's kernel launches are what it removes).
 
 One JSON line: `value` is decode tokens/s of the whole step (B / median step time); `roofline`
 is the attention kernel's; `detail` holds the whole-step fractions, the other decode workloads
@@ -37,7 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode tokens/s + achieved HBM GB/s & MFMA TFLOP/s (% roofline), 1 GPU"
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
-FLUSH_BYTES = 512 << 20
+FLUSH_BYTES = 1 << 30
 ATTN_SOURCE = os.path.join(ROOT, "mla_latent_kv_compress_amd", "csrc", "k_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_{}_traffic.json")
 DETAIL_WORKLOADS = ("lite_bf16", "dsv2_128k", "dsv2_mixed_fp8")
@@ -127,27 +133,50 @@ def gpu_info(torch):
 
 
 def stream_bandwidth(torch, nbytes=4 << 30, reps=5):
-    """Device copy of `nbytes` (read + write) and a read-only reduction over the same bytes."""
+    """Read bandwidth of the library's plain stream-read kernel over `nbytes` (more than the caches
+    hold, read after a sweep of another buffer), and a torch device copy (read + write)."""
+    from mla_latent_kv_compress_amd import api
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flush = Flusher(torch)
     dst.copy_(src)
-    src.sum()
+    api.stream_read(src, sink)
     torch.cuda.synchronize()
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     cp, rd = [], []
     for _ in range(reps):
+        flush()
         e[0].record()
-        dst.copy_(src)
+        api.stream_read(src, sink)
         e[1].record()
-        s = src.sum()
+        flush()
         e[2].record()
+        dst.copy_(src)
+        e[3].record()
         torch.cuda.synchronize()
-        cp.append(e[0].elapsed_time(e[1]))
-        rd.append(e[1].elapsed_time(e[2]))
-    del src, dst, s
+        rd.append(e[0].elapsed_time(e[1]))
+        cp.append(e[2].elapsed_time(e[3]))
+    del src, dst, sink, flush
     torch.cuda.empty_cache()
-    return {"copy_gbps": 2 * nbytes / (min(cp) * 1e-3) / 1e9, "read_gbps": nbytes / (min(rd) * 1e-3) / 1e9,
-            "bytes": nbytes, "method": "torch device copy (read + write) and fp32 sum (read), best of 5"}
+    rd.sort()
+    cp.sort()
+    return {"read_gbps": nbytes / (rd[len(rd) // 2] * 1e-3) / 1e9, "copy_gbps": 2 * nbytes / (cp[len(cp) // 2] * 1e-3) / 1e9,
+            "bytes": nbytes, "method": "mla_stream_read (read only) and torch device copy (read + write), "
+                                       "median of 5, each after a 1 GiB read sweep"}
+
+
+class Flusher:
+    """Evicts the caches by reading FLUSH_BYTES through the stream-read kernel (clean lines only)."""
+
+    def __init__(self, torch):
+        from mla_latent_kv_compress_amd import api
+        self.api = api
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        self.api.stream_read(self.buf, self.sink)
 
 
 def workload_work(wl, ctx):
@@ -163,10 +192,11 @@ def workload_work(wl, ctx):
     uk_uv = H * (s.qk_nope_head_dim + s.v_head_dim) * s.kv_lora_rank
     qpath = (s.q_lora_rank * D + H * s.qk_head_dim * s.q_lora_rank) if s.q_lora_rank else H * s.qk_head_dim * D
     kv_a = s.row_width * D
+    o_proj = D * H * s.v_head_dim
     core_bytes = attn_bytes + uk_uv * asz
     core_flops = attn_flops + B * 2.0 * uk_uv
-    step_bytes = core_bytes + (qpath + kv_a) * asz
-    step_flops = core_flops + B * 2.0 * (qpath + kv_a)
+    step_bytes = core_bytes + (qpath + kv_a + o_proj) * asz
+    step_flops = core_flops + B * 2.0 * (qpath + kv_a + o_proj)
     return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, core_bytes=core_bytes, core_flops=core_flops,
                 step_bytes=step_bytes, step_flops=step_flops)
 
@@ -180,15 +210,15 @@ def measure_decode(name, steps, warmup, flush, splits=None, keep=False):
 
     wl = configs.WORKLOADS[name]
     t_setup = time.perf_counter()
-    layer = Layer(wl.shape, wl.act_dtype, wl.cache_dtype, out_dtype="f32")
+    layer = Layer(wl.shape, wl.act_dtype, wl.cache_dtype, out_dtype="f32", o_proj=True)
     batch = DecodeBatch(layer, wl)
     B = len(batch.hist)
     max_blocks = batch.table.shape[1]
     if splits is None:
         splits = wl.num_splits or api.decode_num_splits(layer.cfg, B, max_blocks)
     ws = torch.empty(api.decode_workspace_size(layer.cfg, B, max_blocks, splits), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, wl.shape.num_heads, wl.shape.v_head_dim), dtype=torch.float32, device="cuda")
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if flush else None
+    out = torch.empty(api.out_shape(layer.cfg, layer.w, B), dtype=torch.float32, device="cuda")
+    scratch = Flusher(torch) if flush else None
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     print(f"setup {setup_s:.1f} s: {name} B={B} splits={splits}", file=sys.stderr, flush=True)
@@ -204,7 +234,7 @@ def measure_decode(name, steps, warmup, flush, splits=None, keep=False):
     marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
         if flush:
-            scratch.fill_(i & 0xFF)
+            scratch()
         marks[i][0].record()
         step()
         marks[i][1].record()
@@ -214,7 +244,7 @@ def measure_decode(name, steps, warmup, flush, splits=None, keep=False):
     pairs = [(ev.create(), ev.create()) for _ in range(steps)]
     for i in range(steps):
         if flush:
-            scratch.fill_(i & 0xFF)
+            scratch()
         step(events=pairs[i])
     torch.cuda.synchronize()
     attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
@@ -227,6 +257,33 @@ def measure_decode(name, steps, warmup, flush, splits=None, keep=False):
         step()
     torch.cuda.synchronize()
     b2b_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # pass 4: the same step captured once in a HIP graph and replayed, flushed as in pass 1
+    # (the graph holds the step's kernels only; the flush runs eagerly between replays)
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        gmarks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            if flush:
+                scratch()
+            gmarks[i][0].record()
+            g.replay()
+            gmarks[i][1].record()
+        torch.cuda.synchronize()
+        graph_ms = stats([a.elapsed_time(b) for a, b in gmarks])
+        del g
+    except Exception as e:                         # reported, not fatal: the eager step is the headline
+        graph_ms = {"error": str(e)}
 
     ctx = batch.ctx.astype(np.int64)
     work = workload_work(wl, ctx)
@@ -239,6 +296,8 @@ def measure_decode(name, steps, warmup, flush, splits=None, keep=False):
         "cache_dtype": wl.cache_dtype, "setup_s": setup_s, "caches_evicted_between_steps": bool(flush),
         "step_ms": st, "decode_tokens_per_s": B / med_s,
         "back_to_back_ms_per_step": b2b_ms, "back_to_back_tokens_per_s": B / (b2b_ms * 1e-3),
+        "graph_step_ms": graph_ms,
+        "graph_tokens_per_s": (B / (graph_ms["median"] * 1e-3)) if graph_ms and "median" in graph_ms else None,
         "attn_ms": at,
         "attn_alg_bytes": work["attn_bytes"], "attn_alg_flops": work["attn_flops"],
         "attn_hbm_gbps": work["attn_bytes"] / attn_mean_s / 1e9,

@@ -112,7 +112,14 @@ typedef struct mla_config {
 } mla_config;
 
 /* Weight pointers (device, act_dtype).  With q_lora_rank == 0, q_b_proj is q_proj
- * [num_heads * (nope + rope), hidden] and q_a_proj / q_a_norm are ignored. */
+ * [num_heads * (nope + rope), hidden] and q_a_proj / q_a_norm are ignored.
+ * o_proj is optional: the output projection that takes the attention result back to the model
+ * width (page "DeepSeek-Coder-V2的MLA多头潜在注意力深度解析", section "MLA 的两个核心部件": the
+ * forward flow ends with the attention result leaving as the layer's output; the pages name no
+ * projection, so its form is a reading: a linear layer whose input is the heads' outputs side by
+ * side in head order, head h at inputs h * v_head_dim .. h * v_head_dim + v_head_dim - 1).
+ * With o_proj NULL, mla_decode and mla_prefill return the per-head outputs [tokens, num_heads,
+ * v_head_dim]; with it set they return o_proj applied to them, [tokens, hidden_size]. */
 typedef struct mla_weights {
   const void *q_a_proj;   /* [q_lora_rank, hidden]                      */
   const void *q_a_norm;   /* [q_lora_rank]                              */
@@ -120,6 +127,7 @@ typedef struct mla_weights {
   const void *kv_a_proj;  /* [kv_lora_rank + rope, hidden]  (kv_a_proj_with_mqa) */
   const void *kv_a_norm;  /* [kv_lora_rank]                             */
   const void *kv_b_proj;  /* [num_heads * (nope + v), kv_lora_rank]     */
+  const void *o_proj;     /* [hidden, num_heads * v], or NULL           */
 } mla_weights;
 
 typedef struct mla_cache {
@@ -147,6 +155,11 @@ int mla_compress_append(const mla_config *cfg, const mla_weights *w, const void 
 
 /* ---------------------------------------------------------------------------------------
  * mla_decode: one decode step for a batch of sequences, weight-absorbed form.
+ * Page "DeepSeek-Coder-V2的MLA多头潜在注意力深度解析", section "MLA 的两个核心部件" (keys and
+ * values of every head are decompressed from the one cached latent by kv_b_proj, the shared
+ * RoPE key joins every head's key) and its FAQ Q2 (all heads read the same cached row): since
+ * kv_b_proj is linear, q_nope is folded through W_UK so each head scores the cached rows
+ * directly, and the softmax-weighted latent is mapped through W_UV afterwards.
  * The new token of sequence b is at position context_lens[b] - 1; it is compressed and
  * written to its slot (block_table[b][pos / 64] * 64 + pos % 64) first, then its query
  * attends to all context_lens[b] cached rows of the sequence (itself included).
@@ -156,7 +169,8 @@ int mla_compress_append(const mla_config *cfg, const mla_weights *w, const void 
  *   num_splits    0 = chosen by the library (mla_decode_num_splits), else 1..1024: each
  *                 sequence's pages are cut into num_splits contiguous ranges whose partial
  *                 softmax states are merged by log-sum-exp
- *   out           [batch, num_heads, v_head_dim] out_dtype
+ *   out           [batch, num_heads, v_head_dim] out_dtype, or [batch, hidden_size] with
+ *                 w->o_proj set
  */
 int32_t mla_decode_num_splits(const mla_config *cfg, int32_t batch, int32_t max_blocks);
 size_t mla_decode_workspace_size(const mla_config *cfg, int32_t batch, int32_t max_blocks,
@@ -207,7 +221,8 @@ int mla_decode_noalloc(const mla_config *cfg, const mla_weights *w, const void *
  *                 0 .. start_pos[s]-1 must already be in the cache
  *   max_q_len     >= every chunk length;  max_ctx >= every start_pos[s] + chunk length,
  *                 and max_ctx <= max_blocks * 64
- *   out           [total_tokens, num_heads, v_head_dim] out_dtype
+ *   out           [total_tokens, num_heads, v_head_dim] out_dtype, or [total_tokens,
+ *                 hidden_size] with w->o_proj set
  */
 size_t mla_prefill_workspace_size(const mla_config *cfg, int32_t num_seqs, int32_t total_tokens,
                                   int32_t max_q_len, int32_t max_ctx);
@@ -230,6 +245,16 @@ int mla_prefill(const mla_config *cfg, const mla_weights *w, const void *hidden,
  */
 int mla_fp8_e4m3_encode(const float *x, uint8_t *codes, int64_t n, void *stream);
 int mla_fp8_e4m3_decode(const uint8_t *codes, float *x, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * mla_stream_read: a measurement reference, not part of the method.  Reads `bytes` (a multiple
+ * of 16) from device memory at `src` (16-byte aligned) once, coalesced, and discards them
+ * (`sink`: 4 device bytes the kernel may write), so the kernel's duration gives the read
+ * bandwidth this GPU reaches for a plain sequential stream; the attention's algorithmic
+ * bandwidth is quoted against it beside the published peak.  Asynchronous on `stream`.
+ * Returns MLA_ERR_INVALID_ARG for a misaligned or null argument.
+ */
+int mla_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 /* Static text for a status code. */
 const char *mla_status_string(int status);

@@ -39,7 +39,7 @@ class MlaConfig(ctypes.Structure):
 
 class MlaWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("q_a_proj", "q_a_norm", "q_b_proj", "kv_a_proj", "kv_a_norm", "kv_b_proj")]
+                ("q_a_proj", "q_a_norm", "q_b_proj", "kv_a_proj", "kv_a_norm", "kv_b_proj", "o_proj")]
 
 
 class MlaCache(ctypes.Structure):
@@ -62,6 +62,7 @@ SIGNATURES = {
     "mla_fp8_e4m3_decode": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
     "mla_decode_noalloc": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                           _i32, _vp, _vp]),
+    "mla_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
     "mla_prefill_workspace_size": (_sz, [_P(MlaConfig), _i32, _i32, _i32, _i32]),
     "mla_prefill": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                    _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
@@ -122,7 +123,13 @@ def make_weights(w):
     """MlaWeights from a dict of device tensors (q_proj may stand in for q_b_proj)."""
     q_b = w.get("q_b_proj", w.get("q_proj"))
     return MlaWeights(*[_ptr(x) for x in (w.get("q_a_proj"), w.get("q_a_norm"), q_b,
-                                         w["kv_a_proj"], w["kv_a_norm"], w["kv_b_proj"])])
+                                         w["kv_a_proj"], w["kv_a_norm"], w["kv_b_proj"], w.get("o_proj"))])
+
+
+def out_shape(cfg, weights, tokens):
+    """Shape of decode / prefill output: [tokens, hidden] with o_proj, else [tokens, H, v_head_dim]."""
+    has_o = (weights.o_proj is not None) if isinstance(weights, MlaWeights) else weights.get("o_proj") is not None
+    return (tokens, cfg.hidden_size) if has_o else (tokens, cfg.num_heads, cfg.v_head_dim)
 
 
 class Cache:
@@ -183,9 +190,9 @@ def decode(cfg, weights, hidden, context_lens, block_table, cache, num_splits=0,
     B, max_blocks = block_table.shape
     nbytes = L.mla_decode_workspace_size(ctypes.byref(cfg), B, max_blocks, num_splits)
     ws = _workspace(nbytes, hidden.device, workspace)
-    if out is None:
-        out = torch.empty((B, cfg.num_heads, cfg.v_head_dim), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
     W = weights_struct if weights_struct is not None else make_weights(weights)
+    if out is None:
+        out = torch.empty(out_shape(cfg, W, B), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
     cs = cache.struct()
     if attn_events is None:
         _check(L.mla_decode(ctypes.byref(cfg), ctypes.byref(W), _ptr(hidden), _ptr(context_lens),
@@ -203,9 +210,9 @@ def decode_noalloc(cfg, weights, hidden, context_lens, block_table, cache, num_s
     """mla_decode_noalloc: the decode step on the library's static per-GPU workspace."""
     L = lib()
     B, max_blocks = block_table.shape
-    if out is None:
-        out = torch.empty((B, cfg.num_heads, cfg.v_head_dim), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
     W = make_weights(weights)
+    if out is None:
+        out = torch.empty(out_shape(cfg, W, B), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
     cs = cache.struct()
     _check(L.mla_decode_noalloc(ctypes.byref(cfg), ctypes.byref(W), _ptr(hidden), _ptr(context_lens),
                                 _ptr(block_table), max_blocks, ctypes.byref(cs), B, num_splits, _ptr(out),
@@ -224,12 +231,18 @@ def prefill(cfg, weights, hidden, cu_seqlens, start_pos, block_table, cache, max
     S, max_blocks = block_table.shape
     nbytes = L.mla_prefill_workspace_size(ctypes.byref(cfg), S, T, max_q_len, max_ctx)
     ws = _workspace(nbytes, hidden.device, workspace)
-    if out is None:
-        out = torch.empty((T, cfg.num_heads, cfg.v_head_dim), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
     W = make_weights(weights)
+    if out is None:
+        out = torch.empty(out_shape(cfg, W, T), dtype=TORCH_OUT[cfg.out_dtype], device=hidden.device)
     cs = cache.struct()
     _check(L.mla_prefill(ctypes.byref(cfg), ctypes.byref(W), _ptr(hidden), _ptr(cu_seqlens), _ptr(start_pos),
                          _ptr(block_table), max_blocks, ctypes.byref(cs), S, T, max_q_len, max_ctx, _ptr(ws),
                          nbytes, _ptr(out), _stream(stream)),
            "mla_prefill")
     return out
+
+
+def stream_read(src, sink, stream=None):
+    """mla_stream_read: read all of `src` (a contiguous device tensor) once and discard it."""
+    _check(lib().mla_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "mla_stream_read")

@@ -77,16 +77,16 @@ __global__ __launch_bounds__(256) void decode_attn_simt_kernel(
   }
 }
 
-void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st) {
+bool launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st) {
   if (act == K_F32) {
     size_t sh = size_t(a.dc + a.dr + 256) * sizeof(float) + 256 * sizeof(long);
     hipLaunchKernelGGL(decode_attn_simt_kernel, dim3(a.H, a.splits, a.B), dim3(256), sh, st, a.H, a.dc,
                        a.dr, a.splits, a.max_blocks, static_cast<const float*>(a.qhat),
                        static_cast<const float*>(a.cache), a.block_table, a.ctx, static_cast<float*>(a.part_o),
                        a.part_ml);
-    return;
+    return true;
   }
-  launch_decode_attn_v2(cache, a, st);           // every bf16-path shape (d_c 512, d_r 64, H % 16 == 0)
+  return launch_decode_attn_v2(cache, a, st);    // every bf16-path shape (d_c 512, d_r 64, H % 16 == 0)
 }
 
 // ==================================================================== prefill, fp32 SIMT
@@ -151,16 +151,16 @@ __global__ __launch_bounds__(256) void prefill_attn_simt_kernel(
   }
 }
 
-void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st) {
+bool launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st) {
   if (act == K_F32) {
     size_t sh = size_t(a.dn + a.dr + 256) * sizeof(float);
     hipLaunchKernelGGL(prefill_attn_simt_kernel, dim3(a.max_q, a.H, a.S), dim3(256), sh, st, a.H, a.dn,
                        a.dr, a.dv, a.dc, a.max_ctx, a.cu, a.start, static_cast<const float*>(a.qs),
                        static_cast<const float*>(a.kv), static_cast<const float*>(a.lat),
                        static_cast<float*>(a.out));
-    return;
+    return true;
   }
-  launch_prefill_attn_fa(a, st);                 // every bf16-path shape (nope 128, rope 64, v 128)
+  return launch_prefill_attn_fa(a, st);          // every bf16-path shape (nope 128, rope 64, v 128)
 }
 
 }  // namespace mla

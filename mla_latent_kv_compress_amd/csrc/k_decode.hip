@@ -92,7 +92,7 @@ constexpr int kKS = kDW / 32;                         // 18 score K steps
 constexpr int kHeads = 64;                            // heads per work-group
 constexpr int kPBytes = kHeads * kStage * 2;          // 4096
 constexpr float kSlack = 64.0f;
-constexpr int kChecked = 0, kMaxOnly = 1, kFixed = 2;     // pass kinds
+constexpr int kChecked = 0, kFixed = 2;                   // pass kinds
 constexpr int kScoreRing = 5;                         // score operand fragments in flight + 1
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

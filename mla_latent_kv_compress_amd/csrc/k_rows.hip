@@ -581,6 +581,49 @@ __global__ __launch_bounds__(256) void fp8_decode_kernel(const uint8_t* __restri
     x[i] = e4m3_to_f(codes[i]);
 }
 
+// ------------------------------------------------------------------ K-split sum
+// out[i] = sum over s of acc[s * n + i], i < n, stored as OutT.
+template <typename OutT>
+__global__ __launch_bounds__(256) void sum_splits_kernel(long n, int nsplit, const float* __restrict__ acc,
+                                                         OutT* __restrict__ out) {
+  for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n; i += long(gridDim.x) * 256) {
+    float t = acc[i];
+    for (int s = 1; s < nsplit; ++s) t += acc[long(s) * n + i];
+    stf<OutT>(out, i, t);
+  }
+}
+
+void launch_sum_splits(int out_type, long n, int nsplit, const float* acc, void* out, hipStream_t st) {
+  if (n <= 0) return;
+  const long blocks = std::min<long>((n + 255) / 256, 2048);
+  if (out_type == K_BF16)
+    hipLaunchKernelGGL(sum_splits_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(256), 0, st, n, nsplit, acc,
+                       static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL(sum_splits_kernel<float>, dim3(unsigned(blocks)), dim3(256), 0, st, n, nsplit, acc,
+                       static_cast<float*>(out));
+}
+
+// ------------------------------------------------------------------ stream-read reference
+// Reads n16 16-byte words once (grid-stride, four loads in flight per lane) and keeps only an
+// XOR of them, so the kernel's time is that of reading the bytes from memory.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, long n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  const long stride = long(gridDim.x) * 256;
+  long i = long(blockIdx.x) * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) acc ^= p[i].x ^ p[i].y ^ p[i].z ^ p[i].w;
+  if (acc == 0x9E3779B9u) sink[0] = acc;           // keeps the loads; almost never stores
+}
+
+void launch_stream_read(const void* p, long n16, uint32_t* sink, hipStream_t st) {
+  if (n16 <= 0) return;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(1024), dim3(256), 0, st, static_cast<const uint4*>(p), n16, sink);
+}
+
 void launch_fp8_codec(bool encode, const void* in, void* out, long n, hipStream_t st) {
   if (n <= 0) return;
   const long blocks = std::min<long>((n + 255) / 256, 4096);

@@ -182,6 +182,15 @@ int mla_fp8_e4m3_decode(const uint8_t* codes, float* x, int64_t n, void* stream)
   return finish();
 }
 
+int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes % 16 != 0 || (bytes > 0 && (!src || !sink)) || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (bytes == 0) return MLA_OK;
+  (void)hipGetLastError();
+  launch_stream_read(src, long(bytes / 16), sink, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
 const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "ok";
@@ -308,24 +317,50 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   a.part_ml = reinterpret_cast<float*>(at(workspace, p.off_part_ml));
   a.order = p.ordered ? reinterpret_cast<int32_t*>(at(workspace, p.off_order)) : nullptr;
   if (ev_attn_begin) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_begin), s);
-  launch_decode_attn(act, kdt(cfg->cache_dtype), a, s);
+  if (!launch_decode_attn(act, kdt(cfg->cache_dtype), a, s)) return MLA_ERR_UNSUPPORTED;
   if (ev_attn_end) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_end), s);
 
   float* otilde = reinterpret_cast<float*>(at(workspace, p.off_otilde));
-  // out[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  The bf16 path
+  // With o_proj the attention output goes to the workspace first: fp32 when the o_proj product
+  // can take it as a bf16 hi + lo pair (skinny kernel), else bf16.
+  const int out_type = kdt(cfg->out_dtype);
+  const long nv = long(d.H) * d.dv;
+  GemmArgs go;
+  int attn_type = out_type;
+  void* attn = out;
+  if (w->o_proj) {
+    attn = at(workspace, p.off_attn);
+    const bool direct = p.split_o.n == 1;
+    go = gemm(path, false, direct ? out_type : K_F32, B, d.D, int(nv), p.split_o, 1, attn, nv, 0, w->o_proj, nv, 0,
+              direct ? out : at(workspace, p.off_o_acc), d.D, 0);
+    if (path == PATH_BF16) {
+      go.xf32 = true;
+      if (!launch_gemm_skinny_ok(go)) go.xf32 = false;
+      attn_type = go.xf32 ? K_F32 : K_BF16;
+    } else {
+      attn_type = K_F32;
+    }
+  }
+  // attn[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  The bf16 path
   // merges the split partials inside the projection kernel (its shape checks admit only the
   // d_c 512, d_v 128 it requires).
   if (path == PATH_BF16) {
-    if (!launch_decode_merge_uv(kdt(cfg->out_dtype), B, d.H, d.dc, d.dn, d.dv, p.splits,
-                                static_cast<const uint16_t*>(a.part_o), a.part_ml, w->kv_b_proj, out, s, otilde,
+    if (!launch_decode_merge_uv(attn_type, B, d.H, d.dc, d.dn, d.dv, p.splits,
+                                static_cast<const uint16_t*>(a.part_o), a.part_ml, w->kv_b_proj, attn, s, otilde,
                                 reinterpret_cast<float*>(at(workspace, p.off_ml1))))
       return MLA_ERR_UNSUPPORTED;
-    return finish();
+  } else {
+    launch_decode_merge(B, d.H, d.dc, p.splits, static_cast<const float*>(a.part_o), a.part_ml, otilde, s);
+    const char* w_uv = static_cast<const char*>(w->kv_b_proj) + size_t(d.dn) * d.dc * asz;
+    launch_gemm(gemm(path, false, attn_type, B, d.dv, d.dc, whole(d.dc), d.H, otilde, long(d.H) * d.dc, d.dc,
+                     w_uv, d.dc, long(d.dkv()) * d.dc, attn, nv, d.dv), s);
   }
-  launch_decode_merge(B, d.H, d.dc, p.splits, static_cast<const float*>(a.part_o), a.part_ml, otilde, s);
-  const char* w_uv = static_cast<const char*>(w->kv_b_proj) + size_t(d.dn) * d.dc * asz;
-  launch_gemm(gemm(path, false, kdt(cfg->out_dtype), B, d.dv, d.dc, whole(d.dc), d.H, otilde, long(d.H) * d.dc, d.dc,
-                   w_uv, d.dc, long(d.dkv()) * d.dc, out, long(d.H) * d.dv, d.dv), s);
+  if (w->o_proj) {
+    // out[b] = o_proj [attn[b][0] | ... | attn[b][H-1]]: K-split partials summed by a second kernel
+    launch_gemm(go, s);
+    if (p.split_o.n > 1)
+      launch_sum_splits(out_type, long(B) * d.D, p.split_o.n, static_cast<const float*>(go.Y), out, s);
+  }
   return finish();
 }
 
@@ -441,7 +476,17 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
   a.max_q = max_q_len; a.max_ctx = max_ctx; a.out_type = kdt(cfg->out_dtype);
   a.cu = cu_seqlens; a.start = start_pos;
   a.qs = qs; a.kv = kv; a.lat = lat; a.kpe = kpe; a.out = out;
-  launch_prefill_attn(act, a, s);
+  if (w->o_proj) {
+    // attention output in act dtype to the workspace, then out = o_proj [heads side by side]
+    a.out = at(workspace, p.off_attn);
+    a.out_type = act;
+  }
+  if (!launch_prefill_attn(act, a, s)) return MLA_ERR_UNSUPPORTED;
+  if (w->o_proj) {
+    const long nv = long(d.H) * d.dv;
+    launch_gemm(gemm(path, false, kdt(cfg->out_dtype), T, d.D, int(nv), whole(int(nv)), 1, a.out, nv, 0, w->o_proj,
+                     nv, 0, out, d.D, 0), s);
+  }
   return finish();
 }
 

@@ -106,7 +106,8 @@ struct DecodeAttnArgs {
   float* part_ml;
   int32_t* order = nullptr;   // [B] scratch: sequences by length, longest first (64-head kernel)
 };
-void launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st);
+// False (nothing launched) when no kernel takes the shape.
+bool launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t st);
 // 64-head work-groups over a bf16 or fp8 cache (k_decode.hip); false if the shape does not apply.
 // With a.order set, a first kernel ranks the sequences by context length (a.B <= kOrderMax) and
 // the work-groups take them longest first.
@@ -144,12 +145,17 @@ struct PrefillAttnArgs {
   const void* kpe;           // [S][max_ctx][dr] fp16 copy of k_pe (bf16 path)
   void* out;                 // [T][H][dv] out_type
 };
-void launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st);
+// False (nothing launched) when no kernel takes the shape.
+bool launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st);
 // Flash-style causal prefill attention (k_prefill.hip), bf16 path with nope 128, rope 64, v 128,
 // d_c 512; false if the shape does not apply.
 bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st);
 
 // Elementwise e4m3fn codec of the fp8 cache: encode fp32 -> codes, or decode codes -> fp32.
 void launch_fp8_codec(bool encode, const void* in, void* out, long n, hipStream_t st);
+// out[i] = sum over the nsplit slices of acc ([nsplit][n] fp32), stored fp32 or bf16 per out_type.
+void launch_sum_splits(int out_type, long n, int nsplit, const float* acc, void* out, hipStream_t st);
+// Reads n16 16-byte words and discards them (a reference for the achievable read bandwidth).
+void launch_stream_read(const void* p, long n16, uint32_t* sink, hipStream_t st);
 
 }  // namespace mla

@@ -166,8 +166,17 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   // (with many splits per sequence every work-group is short and their order matters little)
   p->ordered = hpg == 64 && B <= kOrderMax && p->splits <= 8 && long(B) * p->splits * cdiv(d.H, hpg) > kDecodeRound;
   p->off_order = L.take(size_t(B) * 4);
-  p->off_otilde = L.take(size_t(B) * d.H * d.dc * 4);
+  // o_proj: its K-split partials share the merged-state region (dead once W_UV has read it), and
+  // the attention output reuses the query region (dead once the attention has run) when it fits
+  p->split_o = gemm_splitk(B, d.D, long(d.H) * d.dv, 64, 64);
+  const size_t otilde_bytes = size_t(B) * d.H * d.dc * 4;
+  const size_t oacc_bytes = p->split_o.n > 1 ? size_t(p->split_o.n) * B * d.D * 4 : 0;
+  p->off_otilde = L.take(otilde_bytes > oacc_bytes ? otilde_bytes : oacc_bytes);
+  p->off_o_acc = p->off_otilde;
   p->off_ml1 = L.take(size_t(B) * d.H * 2 * 4);
+  const size_t attn_bytes = size_t(B) * d.H * d.dv * 4;
+  const size_t qhat_bytes = size_t(B) * d.H * d.W() * act;
+  p->off_attn = attn_bytes <= qhat_bytes ? p->off_qhat : L.take(attn_bytes);
   p->bytes = L.top;
   return MLA_OK;
 }
@@ -187,6 +196,7 @@ int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx,
   p->off_tscale = L.take(path == PATH_BF16 && d.cache_dt == MLA_FP8_E4M3 ? size_t(S) * max_ctx * 4 : 0);
   p->q16 = path == PATH_BF16 && d.dq > 0 && d.dq % 64 == 0 && p->q.direct;
   p->off_wq16 = L.take(p->q16 ? size_t(d.H) * d.dqk() * d.dq * 2 : 0);
+  p->off_attn = L.take(size_t(T) * d.H * d.dv * act);
   p->bytes = L.top;
   return MLA_OK;
 }

@@ -92,6 +92,13 @@ struct DecodePlan {
   size_t off_part_ml;         // fp32 [B][splits][H][2]
   size_t off_otilde;          // fp32 [B][H][dc]: the merged state (many splits on the bf16 path)
   size_t off_ml1;             // fp32 [B][H][2]: merged state (0, 1) when the splits are merged first
+  // Output projection (taken only when the weights carry o_proj; the regions are always planned,
+  // inside regions that are dead by then):
+  SplitK split_o;             // K split of the o_proj product (M = B, N = D, K = H * dv)
+  size_t off_attn;            // fp32 [B][H][dv] attention output (bf16 when the fp32 input form
+                              // does not apply): inside the qhat region when it fits
+  size_t off_o_acc;           // fp32 [split_o.n][B][D] o_proj partials (split_o.n > 1): the
+                              // otilde region, sized for both
   size_t bytes;
 };
 int auto_splits(const Dims& d, Path path, int B, int max_blocks);
@@ -110,6 +117,7 @@ struct PrefillPlan {
   size_t off_wq16;            // fp16 copy of q_b_proj (bf16 path with a query LoRA, q16)
   bool q16;                   // bf16 path, dq > 0, dq % 64 == 0: the normed query latent and
                               // q_b_proj enter the q_b projection in fp16
+  size_t off_attn;            // act [T][H][dv] attention output before o_proj (weights with o_proj)
   size_t bytes;
 };
 int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, PrefillPlan* p);

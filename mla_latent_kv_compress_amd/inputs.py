@@ -22,6 +22,7 @@ STREAM_DECODE_X = 1
 STREAM_PAGES = 2
 STREAM_LENGTHS = 3
 STREAM_GAMMA = 5
+STREAM_OPROJ = 6
 STREAM_HISTORY = 1000        # + sequence index
 STREAM_PREFILL = 500000      # + sequence index
 HISTORY_BLOCK = 4096         # history hidden states are drawn in blocks of this many tokens
@@ -42,8 +43,10 @@ def to_dtype_values(x32, dtype):
     raise ValueError(dtype)
 
 
-def make_weights(shape, act_dtype, seed=0, gamma="one"):
-    """Weights in (out, in) layout as float32 arrays of act_dtype values, keyed by name."""
+def make_weights(shape, act_dtype, seed=0, gamma="one", o_proj=False):
+    """Weights in (out, in) layout as float32 arrays of act_dtype values, keyed by name; with
+    o_proj also the output projection [hidden, H * v_head_dim] (from a stream of its own, so the
+    other weights do not depend on whether it is drawn)."""
     g = rng(seed, STREAM_WEIGHTS)
     gg = rng(seed, STREAM_GAMMA)
     out = {}
@@ -56,6 +59,10 @@ def make_weights(shape, act_dtype, seed=0, gamma="one"):
         else:
             v = g.standard_normal(shp, dtype=np.float32) * np.float32(0.02)
         out[name] = to_dtype_values(v, act_dtype)
+    if o_proj:
+        v = rng(seed, STREAM_OPROJ).standard_normal((shape.hidden_size, shape.num_heads * shape.v_head_dim),
+                                                    dtype=np.float32) * np.float32(0.02)
+        out["o_proj"] = to_dtype_values(v, act_dtype)
     return out
 
 

@@ -28,13 +28,13 @@ class Layer:
     """Weights of one MLA layer on the device (plus the float32 host copy they came from)."""
 
     def __init__(self, shape, act_dtype, cache_dtype, seed=0, device="cuda", gamma="one", softmax_scale=None,
-                 out_dtype="f32"):
+                 out_dtype="f32", o_proj=False):
         if softmax_scale is not None:
             from dataclasses import replace
             shape = replace(shape, softmax_scale=softmax_scale)
         self.shape, self.act, self.cache_dtype, self.device = shape, act_dtype, cache_dtype, device
         self.cfg = api.make_config(shape, act_dtype, cache_dtype, out_dtype)
-        self.w_host = inputs.make_weights(shape, act_dtype, seed, gamma=gamma)
+        self.w_host = inputs.make_weights(shape, act_dtype, seed, gamma=gamma, o_proj=o_proj)
         self.w = {k: to_device(v, act_dtype, device) for k, v in self.w_host.items()}
         self.w_struct = api.make_weights(self.w)
 

@@ -10,15 +10,16 @@ from mla_latent_kv_compress_amd.workload import DecodeBatch, Layer
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("shape,act,cache", [(DSV2, "bf16", "bf16"), (DSV2, "bf16", "fp8"), (TINY, "f32", "f32")])
-def test_graph_replays_match_eager(shape, act, cache):
-    print(f"graph replay {act}/{cache}", flush=True)
-    layer = Layer(shape, act, cache, seed=11)
+@pytest.mark.parametrize("shape,act,cache,o_proj", [(DSV2, "bf16", "bf16", False), (DSV2, "bf16", "fp8", False),
+                                                    (TINY, "f32", "f32", False), (DSV2, "bf16", "bf16", True)])
+def test_graph_replays_match_eager(shape, act, cache, o_proj):
+    print(f"graph replay {act}/{cache} o_proj {o_proj}", flush=True)
+    layer = Layer(shape, act, cache, seed=11, o_proj=o_proj)
     batch = DecodeBatch(layer, Workload("g", shape, act, cache, decode_batch=3), seed=11, lengths=[70, 300, 1])
     splits = 3
     B, mb = batch.table.shape
     ws = torch.empty(api.decode_workspace_size(layer.cfg, B, mb, splits), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, shape.num_heads, shape.v_head_dim), dtype=torch.float32, device="cuda")
+    out = torch.empty(api.out_shape(layer.cfg, layer.w, B), dtype=torch.float32, device="cuda")
     ref = batch.run(num_splits=splits, out=torch.empty_like(out), workspace=ws).clone()
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
