@@ -232,8 +232,8 @@ struct SkinnyProb {
 // which the absorb kernel rotates.
 constexpr int kOutQSplit = 7;
 
-// Output tile (MR rows x BN columns from column tile nx) of batch-and-split index z.  BN is 64 or
-// 96, MR 64 or 128: a stage holds the X tile (MR rows x 64 k) and the W tile (BN rows x 64 k);
+// Output tile (MR rows x BN columns from column tile nx) of batch-and-split index z.  BN is 64,
+// 96 or 160, MR 64 or 128: a stage holds the X tile (MR rows x 64 k) and the W tile (BN rows x 64 k);
 // whole KiBs of it are filled by one direct-load instruction each (8 bf16 rows of 128 bytes, or
 // 4 fp32 rows of 256 bytes), dealt round-robin to the four waves; wave (wm, wn) computes rows
 // MR / 2 wm .. + MR / 2 and columns BN / 2 wn .. + BN / 2.
@@ -296,7 +296,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
   };
   auto wait_for = [&](int jj) {                         // stage jj landed (this wave's part)
     const int ahead = min(nk - 1, jj + S - 2) - jj;     // later stages already issued
-    static_assert(S <= 7 && 5 * NQ < 64, "wait counts");
+    static_assert(S <= 7 && (S - 2) * NQ < 64, "wait counts");
     switch (ahead) {
       case 5: sk_wait_vm<(S >= 7 ? 5 : 0) * NQ>(); break;
       case 4: sk_wait_vm<(S >= 6 ? 4 : 0) * NQ>(); break;
@@ -654,8 +654,9 @@ bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, 
 // qhat[b][h] = [ W_UK^h^T q_nope[b][h] (bf16, d_c values) | RoPE(q_pe[b][h]) (fp16, d_r values) ]
 // with the softmax scale (times log2 e) folded in.  W_UK^h is rows [h (dn + dv), +dn) of
 // kv_b_proj ([d][c], c contiguous).  Grid (3, H, ceil(B / 64)): blocks x = 0, 1 take latent
-// columns [256 x, 256 x + 256) for 64 decode rows, x = 2 rotates q_pe.  A latent block stages
-// its [128 d x 256 c] slice of W_UK^h in LDS (rows of 512 bytes, 32-byte segment s of row d at
+// columns [256 x, 256 x + 256) for 64 decode rows, x = 2 rotates q_pe.  A latent block first
+// requests its 64 rows of q_nope (into registers: they do not depend on the weight, so the two
+// loads overlap), then stages its [128 d x 256 c] slice of W_UK^h in LDS (rows of 512 bytes, 32-byte segment s of row d at
 // s ^ (d & 15), so the transposing reads of 16 rows hit distinct banks) and reads it with
 // ds_read_b64_tr_b16 as the B operand (8 consecutive d per lane); wave w owns columns
 // 256 x + 64 w .. + 64 and keeps those B fragments in registers while it walks the four 16-row
@@ -698,25 +699,64 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
     return;
   }
   const int c0 = blockIdx.x * kCols;
+  const int li = lane & 15, g = lane >> 4;
+  // The block's queries first (independent of W_UK, so their loads overlap the weight's): lane
+  // (li, g) of M-tile mt holds q_nope[b0 + 16 mt + li][32 ks + 8 g .. + 7], scaled (rows past B
+  // re-read row B - 1; their results are not stored).
+  constexpr int kMt = 4;                              // 16-row tiles: 64 decode rows per block
+  float v[kMt][kKs][8];
+#pragma unroll
+  for (int mt = 0; mt < kMt; ++mt) {
+    const int bl = min(b0 + 16 * mt + li, B - 1);
+    if constexpr (QS) {
+      const float* src = q_nope32 + (long(bl) * H + h) * DN + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        const float4 x0 = *reinterpret_cast<const float4*>(src + 32 * ks);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 32 * ks + 4);
+        v[mt][ks][0] = x0.x; v[mt][ks][1] = x0.y; v[mt][ks][2] = x0.z; v[mt][ks][3] = x0.w;
+        v[mt][ks][4] = x1.x; v[mt][ks][5] = x1.y; v[mt][ks][6] = x1.z; v[mt][ks][7] = x1.w;
+      }
+    } else {
+      // fp32 partials, added in split order, then scaled
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[mt][ks][j] = 0.f;
+      const float* src = qh + long(bl) * nq + 8 * g;
+      for (int sp = 0; sp < nsplit; ++sp) {
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+          const float4 x0 = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks);
+          const float4 x1 = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks + 4);
+          v[mt][ks][0] += x0.x; v[mt][ks][1] += x0.y; v[mt][ks][2] += x0.z; v[mt][ks][3] += x0.w;
+          v[mt][ks][4] += x1.x; v[mt][ks][5] += x1.y; v[mt][ks][6] += x1.z; v[mt][ks][7] += x1.w;
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[mt][ks][j] *= scale;
+    }
+  }
   {
     // W_UK^h[d][c0 .. c0 + 256): 16-byte chunk ch of row d (columns 8 ch .. + 7) at segment
     // (ch >> 1) ^ (d & 15), half ch & 1
     const uint16_t* wsrc = kv_b + long(h) * (DN + dv) * dc + c0;
     constexpr int kChunks = DN * kCols / 8;
-    uint4 v[kChunks / 256];
+    uint4 w[kChunks / 256];
 #pragma unroll
     for (int j = 0; j < kChunks / 256; ++j) {
       const int i = tid + 256 * j, d = i >> 5, ch = i & 31;
-      v[j] = *reinterpret_cast<const uint4*>(wsrc + long(d) * dc + 8 * ch);
+      w[j] = *reinterpret_cast<const uint4*>(wsrc + long(d) * dc + 8 * ch);
     }
 #pragma unroll
     for (int j = 0; j < kChunks / 256; ++j) {
       const int i = tid + 256 * j, d = i >> 5, ch = i & 31;
-      *reinterpret_cast<uint4*>(wt + d * 512 + 32 * ((ch >> 1) ^ (d & 15)) + 16 * (ch & 1)) = v[j];
+      *reinterpret_cast<uint4*>(wt + d * 512 + 32 * ((ch >> 1) ^ (d & 15)) + 16 * (ch & 1)) = w[j];
     }
   }
   __syncthreads();
-  const int li = lane & 15, g = lane >> 4;
   // B fragments of the wave's four 16-column tiles, all K steps: W_UK[32 ks + 8 g + j][c] for
   // c = 64 wave + 16 nt + li: transposing reads of rows d0 .. d0 + 3 (and + 4 .. + 7), lane
   // (li & 3) taking columns 4 (li & 3) .. + 3 of the tile's segment.
@@ -736,47 +776,9 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
       bw[ks][nt] = __builtin_bit_cast(bf16x8_t, bv);
     }
   typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-#pragma unroll 1
-  for (int mt = 0; mt < 4; ++mt) {
-    const int b = b0 + 16 * mt + li;
-    if (b0 + 16 * mt >= B) break;                     // uniform over the wave
-    const int bl = min(b, B - 1);
-    float v[kKs][8];
-    if constexpr (QS) {
-      const float* src = q_nope32 + (long(bl) * H + h) * DN + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        const float4 x0 = *reinterpret_cast<const float4*>(src + 32 * ks);
-        const float4 x1 = *reinterpret_cast<const float4*>(src + 32 * ks + 4);
-        v[ks][0] = x0.x; v[ks][1] = x0.y; v[ks][2] = x0.z; v[ks][3] = x0.w;
-        v[ks][4] = x1.x; v[ks][5] = x1.y; v[ks][6] = x1.z; v[ks][7] = x1.w;
-      }
-    } else {
-      // fp32 partials: every K step's values of one split are requested together (one round
-      // trip per split; the splits are added in order), then scaled
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[ks][j] = 0.f;
-      const float* src = qh + long(bl) * nq + 8 * g;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        float4 x[kKs][2];
-#pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) {
-          x[ks][0] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks);
-          x[ks][1] = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks + 4);
-        }
-#pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) {
-          v[ks][0] += x[ks][0].x; v[ks][1] += x[ks][0].y; v[ks][2] += x[ks][0].z; v[ks][3] += x[ks][0].w;
-          v[ks][4] += x[ks][1].x; v[ks][5] += x[ks][1].y; v[ks][6] += x[ks][1].z; v[ks][7] += x[ks][1].w;
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[ks][j] *= scale;
-    }
+  for (int mt = 0; mt < kMt; ++mt) {
+    if (b0 + 16 * mt >= B) break;                     // uniform over the block
     f32x4_t acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -785,8 +787,8 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
       bf16x8v hi, lo;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        hi[j] = (__bf16)v[ks][j];                       // round to nearest even
-        lo[j] = (__bf16)(v[ks][j] - (float)hi[j]);
+        hi[j] = (__bf16)v[mt][ks][j];                   // round to nearest even
+        lo[j] = (__bf16)(v[mt][ks][j] - (float)hi[j]);
       }
       const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, hi), al = __builtin_bit_cast(bf16x8_t, lo);
 #pragma unroll
@@ -862,6 +864,11 @@ static void launch_skinny(const GemmArgs& g, const SkinnyProb& p, hipStream_t st
   const long z = long(g.batch) * g.nsplit;
 #define MLA_SK(BN, MR, NX) \
   hipLaunchKernelGGL((gemm_skinny_kernel<OUT, BN, MR, XF>), dim3(NX, 1, unsigned(z)), dim3(256), 0, st, p)
+  if (g.bn == 160 && g.N % 160 == 0) {
+    if (g.M <= 64) MLA_SK(160, 64, g.N / 160);
+    else MLA_SK(160, 128, g.N / 160);
+    return;
+  }
   if (g.N % 96 == 0 && (g.N / 96) * z % 256 == 0 && ((g.N + 63) / 64) * z % 256 != 0) {
     if (g.M <= 64) MLA_SK(96, 64, g.N / 96);
     else MLA_SK(96, 128, g.N / 96);

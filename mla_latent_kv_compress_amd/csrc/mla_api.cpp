@@ -321,8 +321,9 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   if (ev_attn_end) (void)hipEventRecord(static_cast<hipEvent_t>(ev_attn_end), s);
 
   float* otilde = reinterpret_cast<float*>(at(workspace, p.off_otilde));
-  // With o_proj the attention output goes to the workspace first: fp32 when the o_proj product
-  // can take it as a bf16 hi + lo pair (skinny kernel), else bf16.
+  // With o_proj the attention output goes to the workspace first, in the activation dtype (bf16:
+  // its rounding moves the projected output by about 2^-9 of its rms, and the weight stream, not
+  // the activation, is what the product should spend its loads on).
   const int out_type = kdt(cfg->out_dtype);
   const long nv = long(d.H) * d.dv;
   GemmArgs go;
@@ -330,16 +331,11 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   void* attn = out;
   if (w->o_proj) {
     attn = at(workspace, p.off_attn);
+    attn_type = act;
     const bool direct = p.split_o.n == 1;
     go = gemm(path, false, direct ? out_type : K_F32, B, d.D, int(nv), p.split_o, 1, attn, nv, 0, w->o_proj, nv, 0,
               direct ? out : at(workspace, p.off_o_acc), d.D, 0);
-    if (path == PATH_BF16) {
-      go.xf32 = true;
-      if (!launch_gemm_skinny_ok(go)) go.xf32 = false;
-      attn_type = go.xf32 ? K_F32 : K_BF16;
-    } else {
-      attn_type = K_F32;
-    }
+    if (p.o_wide) go.bn = 160;
   }
   // attn[b][h] = W_UV^h otilde[b][h]  (W_UV^h = kv_b_proj rows of head h's v).  The bf16 path
   // merges the split partials inside the projection kernel (its shape checks admit only the

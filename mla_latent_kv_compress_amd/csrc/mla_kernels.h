@@ -26,6 +26,8 @@ struct GemmArgs {
   bool f16in = false;        // X and W are fp16 (large-tile kernel only)
   const float* row_scale = nullptr;  // large-tile kernel: output row m of batch z times
   long srs = 0;                      // row_scale[z * srs + m]
+  int bn = 0;                // skinny kernel column tile: 0 chooses 64 or 96; 160 (N % 160 == 0)
+                             // for wide outputs whose K split was planned with it
 };
 void launch_gemm(const GemmArgs& g, hipStream_t st);
 // 256 x 256-tile GEMM (k_gemm_tile.hip) for large TN products with a bf16 or fp16 output and no K

@@ -168,7 +168,19 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   p->off_order = L.take(size_t(B) * 4);
   // o_proj: its K-split partials share the merged-state region (dead once W_UV has read it), and
   // the attention output reuses the query region (dead once the attention has run) when it fits
-  p->split_o = gemm_splitk(B, d.D, long(d.H) * d.dv, 64, 64);
+  const long ko = long(d.H) * d.dv;
+  p->o_wide = path == PATH_BF16 && B <= 128 && d.D % 160 == 0 && ko % 64 == 0 && d.D / 160 <= 256;
+  if (p->o_wide) {
+    // one round of 256 work-groups: D / 160 column tiles times the K split
+    long n = 256 / (d.D / 160);
+    const long most = ko / 256;
+    if (n > most) n = most;
+    if (n < 1) n = 1;
+    const long chunk = rup(cdiv(ko, n), 64);
+    p->split_o = SplitK{int(cdiv(ko, chunk)), int(chunk)};
+  } else {
+    p->split_o = gemm_splitk(B, d.D, ko, 64, 64);
+  }
   const size_t otilde_bytes = size_t(B) * d.H * d.dc * 4;
   const size_t oacc_bytes = p->split_o.n > 1 ? size_t(p->split_o.n) * B * d.D * 4 : 0;
   p->off_otilde = L.take(otilde_bytes > oacc_bytes ? otilde_bytes : oacc_bytes);

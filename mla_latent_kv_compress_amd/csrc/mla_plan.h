@@ -95,8 +95,10 @@ struct DecodePlan {
   // Output projection (taken only when the weights carry o_proj; the regions are always planned,
   // inside regions that are dead by then):
   SplitK split_o;             // K split of the o_proj product (M = B, N = D, K = H * dv)
-  size_t off_attn;            // fp32 [B][H][dv] attention output (bf16 when the fp32 input form
-                              // does not apply): inside the qhat region when it fits
+  bool o_wide;                // o_proj on the skinny kernel's 160-column tiles (bf16 path,
+                              // B <= 128, D % 160 == 0), its split sized for them
+  size_t off_attn;            // [B][H][dv] attention output (bf16 on the bf16 path, fp32 on the
+                              // fp32 path): inside the qhat region when it fits
   size_t off_o_acc;           // fp32 [split_o.n][B][D] o_proj partials (split_o.n > 1): the
                               // otilde region, sized for both
   size_t bytes;
