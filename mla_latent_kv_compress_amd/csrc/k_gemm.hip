@@ -653,28 +653,30 @@ bool launch_decode_merge_uv(int out_type, int B, int H, int dc, int dn, int dv, 
 // ------------------------------------------------------------------ absorb + query RoPE (decode)
 // qhat[b][h] = [ W_UK^h^T q_nope[b][h] (bf16, d_c values) | RoPE(q_pe[b][h]) (fp16, d_r values) ]
 // with the softmax scale (times log2 e) folded in.  W_UK^h is rows [h (dn + dv), +dn) of
-// kv_b_proj ([d][c], c contiguous).  Grid (3, H, ceil(B / 64)): blocks x = 0, 1 take latent
-// columns [256 x, 256 x + 256) for 64 decode rows, x = 2 rotates q_pe.  A latent block first
-// requests its 64 rows of q_nope (into registers: they do not depend on the weight, so the two
-// loads overlap), then stages its [128 d x 256 c] slice of W_UK^h in LDS (rows of 512 bytes, 32-byte segment s of row d at
-// s ^ (d & 15), so the transposing reads of 16 rows hit distinct banks) and reads it with
-// ds_read_b64_tr_b16 as the B operand (8 consecutive d per lane); wave w owns columns
-// 256 x + 64 w .. + 64 and keeps those B fragments in registers while it walks the four 16-row
-// tiles.  The query q_nope (fp32) enters the products as a bf16 pair hi + lo (two MFMAs per
-// fragment), so the latent query carries no bf16 rounding of its input; only the result is
-// rounded (to bf16).  The RoPE part is kept in fp16 (11 significant bits): with the rotary key
-// it scores in an fp16 product, where it would lose three bits in bf16.
+// kv_b_proj ([d][c], c contiguous).  Grid (d_c / KC + 1, H, ceil(B / 64)): blocks x < d_c / KC
+// take latent columns [KC x, KC x + KC) of head h for 64 decode rows, the last x rotates q_pe.
+// A latent block stages its [128 d x KC c] slice of W_UK^h in LDS (rows of 2 KC bytes, 32-byte
+// segment s of row d at s ^ (d mod KC / 16), so the transposing reads of 16 rows spread over the
+// banks) and forms the transposed product C[c][b] = sum_d W_UK[d][c] q[b][d]: W enters as the A
+// operand through ds_read_b64_tr_b16 (8 consecutive d per lane), the query as the B operand.
+// Wave w owns decode rows b0 + 16 w .. + 15 (it loads only its own queries) and every column
+// tile of the block; the C layout leaves four consecutive columns of one row in a lane, stored
+// as one 8-byte write.  The query q_nope (fp32) enters the products as a bf16 pair hi + lo (two
+// MFMAs per fragment), so the latent query carries no bf16 rounding of its input; only the
+// result is rounded (to bf16).  The RoPE part is kept in fp16 (11 significant bits): with the
+// rotary key it scores in an fp16 product, where it would lose three bits in bf16.
 // QS: q_nope arrives as fp32 alpha q [B][H][DN] and q_pe as fp32 q [B][H][dr] (the projection's
 // split epilogue); otherwise q is the sum of nsplit fp32 partials of the projection.
-template <int DN, bool QS>
+template <int DN, int KC, bool QS>
 __global__ __launch_bounds__(256) void absorb_rope_kernel(
     int B, int H, int dr, int dc, int dv, int nsplit, const float* __restrict__ q_acc,
     const float* __restrict__ q_nope32, const float* __restrict__ q_pe32,
     const float* __restrict__ rope_tab, float scale, const uint16_t* __restrict__ kv_b,
     uint16_t* __restrict__ qhat) {
-  constexpr int kCols = 256;                          // latent columns per block
   constexpr int kKs = DN / 32;                        // K steps
-  __shared__ __attribute__((aligned(16))) char wt[DN * kCols * 2];
+  constexpr int kMt = KC / 16;                        // 16-column tiles
+  constexpr int kSeg = KC / 16;                       // 32-byte segments per staged row
+  __shared__ __attribute__((aligned(16))) char wt[DN * KC * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b0 = blockIdx.z * 64;
   const int dqk = DN + dr, W = dc + dr;
@@ -685,126 +687,132 @@ __global__ __launch_bounds__(256) void absorb_rope_kernel(
     for (int sp = 0; sp < nsplit; ++sp) v += qh[sp * sstride + long(b) * nq + i];
     return v;
   };
-  if (blockIdx.x == 2) {                              // RoPE block: fp16 (scale RoPE(q_pe))
+  if (blockIdx.x == gridDim.x - 1) {                  // RoPE block: fp16 (scale RoPE(q_pe))
     const int half = dr / 2;
     for (int e = tid; e < 64 * half; e += 256) {
       const int b = b0 + e / half, pi = e % half;
       if (b >= B) continue;
       const float c = rope_tab[long(b) * dr + pi], sn = rope_tab[long(b) * dr + half + pi];
-      const float* qp = q_pe32 + (long(b) * H + h) * dr + 2 * pi;
-      const float ev = QS ? qp[0] : qsum(b, DN + 2 * pi), ov = QS ? qp[1] : qsum(b, DN + 2 * pi + 1);
+      float ev, ov;
+      if constexpr (QS) {
+        const float* qp = q_pe32 + (long(b) * H + h) * dr + 2 * pi;
+        ev = qp[0];
+        ov = qp[1];
+      } else {
+        ev = qsum(b, DN + 2 * pi);
+        ov = qsum(b, DN + 2 * pi + 1);
+      }
       const uint32_t pr = uint32_t(f2h(scale * (ev * c - ov * sn))) | (uint32_t(f2h(scale * (ev * sn + ov * c))) << 16);
       *reinterpret_cast<uint32_t*>(qhat + (long(b) * H + h) * W + dc + 2 * pi) = pr;
     }
     return;
   }
-  const int c0 = blockIdx.x * kCols;
+  const int c0 = blockIdx.x * KC;
   const int li = lane & 15, g = lane >> 4;
-  // The block's queries first (independent of W_UK, so their loads overlap the weight's): lane
-  // (li, g) of M-tile mt holds q_nope[b0 + 16 mt + li][32 ks + 8 g .. + 7], scaled (rows past B
-  // re-read row B - 1; their results are not stored).
-  constexpr int kMt = 4;                              // 16-row tiles: 64 decode rows per block
-  float v[kMt][kKs][8];
-#pragma unroll
-  for (int mt = 0; mt < kMt; ++mt) {
-    const int bl = min(b0 + 16 * mt + li, B - 1);
+  const int rb = b0 + 16 * wave;                      // the wave's first decode row (a wave past
+                                                      // B still stages its share of the weight)
+  // The wave's queries (B operand): lane (li, g) holds q_nope[rb + li][32 ks + 8 g .. + 7],
+  // scaled; rows past B re-read row B - 1 and are not stored.  Requested before the weight, so
+  // the two loads overlap.
+  float v[kKs][8];
+  {
+    const int bl = min(rb + li, B - 1);
     if constexpr (QS) {
       const float* src = q_nope32 + (long(bl) * H + h) * DN + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks) {
         const float4 x0 = *reinterpret_cast<const float4*>(src + 32 * ks);
         const float4 x1 = *reinterpret_cast<const float4*>(src + 32 * ks + 4);
-        v[mt][ks][0] = x0.x; v[mt][ks][1] = x0.y; v[mt][ks][2] = x0.z; v[mt][ks][3] = x0.w;
-        v[mt][ks][4] = x1.x; v[mt][ks][5] = x1.y; v[mt][ks][6] = x1.z; v[mt][ks][7] = x1.w;
+        v[ks][0] = x0.x; v[ks][1] = x0.y; v[ks][2] = x0.z; v[ks][3] = x0.w;
+        v[ks][4] = x1.x; v[ks][5] = x1.y; v[ks][6] = x1.z; v[ks][7] = x1.w;
       }
     } else {
       // fp32 partials, added in split order, then scaled
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[mt][ks][j] = 0.f;
+        for (int j = 0; j < 8; ++j) v[ks][j] = 0.f;
       const float* src = qh + long(bl) * nq + 8 * g;
       for (int sp = 0; sp < nsplit; ++sp) {
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
           const float4 x0 = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks);
           const float4 x1 = *reinterpret_cast<const float4*>(src + sp * sstride + 32 * ks + 4);
-          v[mt][ks][0] += x0.x; v[mt][ks][1] += x0.y; v[mt][ks][2] += x0.z; v[mt][ks][3] += x0.w;
-          v[mt][ks][4] += x1.x; v[mt][ks][5] += x1.y; v[mt][ks][6] += x1.z; v[mt][ks][7] += x1.w;
+          v[ks][0] += x0.x; v[ks][1] += x0.y; v[ks][2] += x0.z; v[ks][3] += x0.w;
+          v[ks][4] += x1.x; v[ks][5] += x1.y; v[ks][6] += x1.z; v[ks][7] += x1.w;
         }
       }
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[mt][ks][j] *= scale;
+        for (int j = 0; j < 8; ++j) v[ks][j] *= scale;
     }
   }
   {
-    // W_UK^h[d][c0 .. c0 + 256): 16-byte chunk ch of row d (columns 8 ch .. + 7) at segment
-    // (ch >> 1) ^ (d & 15), half ch & 1
+    // W_UK^h[d][c0 .. c0 + KC): 16-byte chunk ch of row d (columns 8 ch .. + 7) at segment
+    // (ch >> 1) ^ (d mod kSeg), half ch & 1
     const uint16_t* wsrc = kv_b + long(h) * (DN + dv) * dc + c0;
-    constexpr int kChunks = DN * kCols / 8;
+    constexpr int kRowCh = KC / 8, kChunks = DN * kRowCh;
+    static_assert(kChunks % 256 == 0, "whole chunks per thread");
     uint4 w[kChunks / 256];
 #pragma unroll
     for (int j = 0; j < kChunks / 256; ++j) {
-      const int i = tid + 256 * j, d = i >> 5, ch = i & 31;
+      const int i = tid + 256 * j, d = i / kRowCh, ch = i % kRowCh;
       w[j] = *reinterpret_cast<const uint4*>(wsrc + long(d) * dc + 8 * ch);
     }
 #pragma unroll
     for (int j = 0; j < kChunks / 256; ++j) {
-      const int i = tid + 256 * j, d = i >> 5, ch = i & 31;
-      *reinterpret_cast<uint4*>(wt + d * 512 + 32 * ((ch >> 1) ^ (d & 15)) + 16 * (ch & 1)) = w[j];
+      const int i = tid + 256 * j, d = i / kRowCh, ch = i % kRowCh;
+      *reinterpret_cast<uint4*>(wt + d * (2 * KC) + 32 * ((ch >> 1) ^ (d % kSeg)) + 16 * (ch & 1)) = w[j];
     }
   }
   __syncthreads();
-  // B fragments of the wave's four 16-column tiles, all K steps: W_UK[32 ks + 8 g + j][c] for
-  // c = 64 wave + 16 nt + li: transposing reads of rows d0 .. d0 + 3 (and + 4 .. + 7), lane
-  // (li & 3) taking columns 4 (li & 3) .. + 3 of the tile's segment.
-  bf16x8_t bw[kKs][4];
-#pragma unroll
-  for (int ks = 0; ks < kKs; ++ks)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      typedef short s16x4v __attribute__((ext_vector_type(4)));
-      const int d0 = 32 * ks + 8 * g + (li >> 2), seg = 4 * wave + nt;
-      const char* p0 = wt + d0 * 512 + 32 * (seg ^ (d0 & 15)) + 8 * (li & 3);
-      const char* p1 = wt + (d0 + 4) * 512 + 32 * (seg ^ ((d0 + 4) & 15)) + 8 * (li & 3);
-      const s16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p0));
-      const s16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p1));
-      typedef short s16x8v __attribute__((ext_vector_type(8)));
-      const s16x8v bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      bw[ks][nt] = __builtin_bit_cast(bf16x8_t, bv);
-    }
+  if (rb >= B) return;                                // uniform over the wave
   typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+  typedef short s16x4v __attribute__((ext_vector_type(4)));
+  typedef short s16x8v __attribute__((ext_vector_type(8)));
+  f32x4_t acc[kMt];
 #pragma unroll
-  for (int mt = 0; mt < kMt; ++mt) {
-    if (b0 + 16 * mt >= B) break;                     // uniform over the block
-    f32x4_t acc[4];
+  for (int mt = 0; mt < kMt; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < kKs; ++ks) {
+    bf16x8v hi, lo;
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      bf16x8v hi, lo;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        hi[j] = (__bf16)v[mt][ks][j];                   // round to nearest even
-        lo[j] = (__bf16)(v[mt][ks][j] - (float)hi[j]);
-      }
-      const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, hi), al = __builtin_bit_cast(bf16x8_t, lo);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[ks][nt], acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[ks][nt], acc[nt], 0, 0, 0);
-      }
+    for (int j = 0; j < 8; ++j) {
+      hi[j] = (__bf16)v[ks][j];                       // round to nearest even
+      lo[j] = (__bf16)(v[ks][j] - (float)hi[j]);
     }
-    // C layout: lane holds C[4 g + r][li] of each 16 x 16 tile.
+    const bf16x8_t qh8 = __builtin_bit_cast(bf16x8_t, hi), ql8 = __builtin_bit_cast(bf16x8_t, lo);
+    // A fragments of this K step: W_UK[32 ks + 8 g + j][c0 + 16 mt + li], transposing reads of
+    // rows d0 .. d0 + 3 (and + 4 .. + 7), lane (li & 3) taking columns 4 (li & 3) .. + 3 of the
+    // tile's segment
+    bf16x8_t aw[kMt];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int mt = 0; mt < kMt; ++mt) {
+      const int d0 = 32 * ks + 8 * g + (li >> 2);
+      const char* p0 = wt + d0 * (2 * KC) + 32 * (mt ^ (d0 % kSeg)) + 8 * (li & 3);
+      const char* p1 = wt + (d0 + 4) * (2 * KC) + 32 * (mt ^ ((d0 + 4) % kSeg)) + 8 * (li & 3);
+      const s16x4v a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p0));
+      const s16x4v a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4v __attribute__((address_space(3)))*)(p1));
+      const s16x8v av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      aw[mt] = __builtin_bit_cast(bf16x8_t, av);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int bo = b0 + 16 * mt + 4 * g + r;
-        if (bo < B) qhat[(long(bo) * H + h) * W + c0 + 64 * wave + 16 * nt + li] = f2bf(acc[nt][r]);
-      }
+    for (int mt = 0; mt < kMt; ++mt) {
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[mt], qh8, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[mt], ql8, acc[mt], 0, 0, 0);
+    }
+  }
+  // C layout: lane holds C[c = 16 mt + 4 g + r][b = rb + li], r = 0..3: four consecutive latent
+  // columns of one row, one 8-byte store
+  const int bo = rb + li;
+  if (bo < B) {
+    uint16_t* dst = qhat + (long(bo) * H + h) * W + c0 + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < kMt; ++mt)
+      *reinterpret_cast<uint2*>(dst + 16 * mt) =
+          make_uint2(uint32_t(f2bf(acc[mt][0])) | (uint32_t(f2bf(acc[mt][1])) << 16),
+                     uint32_t(f2bf(acc[mt][2])) | (uint32_t(f2bf(acc[mt][3])) << 16));
   }
 }
 
@@ -812,15 +820,23 @@ bool launch_absorb_rope(int B, int H, int dn, int dr, int dc, int dv, int nsplit
                         const float* rope_tab, float scale, const void* kv_b, void* qhat, hipStream_t st,
                         const float* q_nope32, const float* q_pe32) {
   if (dn != 128 || dc != 512 || dr % 2 != 0 || B <= 0) return false;
-  dim3 grid(3, H, (B + 63) / 64);
-  if (q_nope32 && q_pe32)
-    hipLaunchKernelGGL((absorb_rope_kernel<128, true>), grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, nullptr,
-                       q_nope32, q_pe32, rope_tab, scale, static_cast<const uint16_t*>(kv_b),
-                       static_cast<uint16_t*>(qhat));
-  else
-    hipLaunchKernelGGL((absorb_rope_kernel<128, false>), grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, q_acc,
-                       nullptr, nullptr, rope_tab, scale, static_cast<const uint16_t*>(kv_b),
-                       static_cast<uint16_t*>(qhat));
+  // 128-column blocks; 64-column ones when there are few heads, so that the blocks still spread
+  // over the CUs
+  const bool narrow = H < 64;
+  const dim3 grid(dc / (narrow ? 64 : 128) + 1, H, (B + 63) / 64);
+  const bool qs = q_nope32 && q_pe32;
+#define MLA_AB(KC, QS)                                                                                   \
+  hipLaunchKernelGGL((absorb_rope_kernel<128, KC, QS>), grid, dim3(256), 0, st, B, H, dr, dc, dv, nsplit, \
+                     QS ? nullptr : q_acc, q_nope32, q_pe32, rope_tab, scale, static_cast<const uint16_t*>(kv_b), \
+                     static_cast<uint16_t*>(qhat))
+  if (narrow) {
+    if (qs) MLA_AB(64, true);
+    else MLA_AB(64, false);
+  } else {
+    if (qs) MLA_AB(128, true);
+    else MLA_AB(128, false);
+  }
+#undef MLA_AB
   return true;
 }
 
