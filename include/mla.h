@@ -109,6 +109,12 @@ typedef struct mla_config {
   float rope_beta_fast;                /* > rope_beta_slow when rope_factor > 1 */
   float rope_beta_slow;                /* >= 0 */
   float rope_mscale;
+  /* mla_prefill decompresses a sequence's cached latents to per-head keys and values in blocks
+   * of this many positions (a multiple of 64), one block after another, so its workspace holds
+   * one block per sequence however long the context; 0 lets the library choose (blocks that
+   * keep the decompressed keys and values of all sequences within 2 GiB, and a single block
+   * when the context fits).  Ignored on the fp32 path, which decompresses the whole context. */
+  int32_t prefill_key_block;
 } mla_config;
 
 /* Weight pointers (device, act_dtype).  With q_lora_rank == 0, q_b_proj is q_proj

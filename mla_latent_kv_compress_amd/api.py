@@ -34,7 +34,7 @@ class MlaConfig(ctypes.Structure):
                 ("cache_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("rope_factor", ctypes.c_float), ("rope_original_max_position", ctypes.c_int32),
                 ("rope_beta_fast", ctypes.c_float), ("rope_beta_slow", ctypes.c_float),
-                ("rope_mscale", ctypes.c_float)]
+                ("rope_mscale", ctypes.c_float), ("prefill_key_block", ctypes.c_int32)]
 
 
 class MlaWeights(ctypes.Structure):

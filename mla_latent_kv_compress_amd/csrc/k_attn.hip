@@ -90,9 +90,10 @@ bool launch_decode_attn(int act, int cache, const DecodeAttnArgs& a, hipStream_t
 }
 
 // ==================================================================== prefill, fp32 SIMT
-// Generic dims.  Grid (max_q, H, S); one query per block, 256 threads over keys.
+// Generic dims.  Grid (max_q, H, S); one query per block, 256 threads over keys; kv and lat hold
+// kb >= max_ctx rows per sequence.
 __global__ __launch_bounds__(256) void prefill_attn_simt_kernel(
-    int H, int dn, int dr, int dv, int dc, int max_ctx, const int32_t* __restrict__ cu,
+    int H, int dn, int dr, int dv, int dc, int kb, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ start, const float* __restrict__ qs, const float* __restrict__ kv,
     const float* __restrict__ lat, float* __restrict__ out) {
   extern __shared__ float sh[];                     // q [dn+dr] | p [256]
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void prefill_attn_simt_kernel(
   float* pbuf = sh + dqk;
   for (int k = tid; k < dqk; k += 256) q[k] = qs[(long(q_begin + i) * H + h) * dqk + k];
   __syncthreads();
-  const long kvb = long(s) * max_ctx;
+  const long kvb = long(s) * kb;                    // kv / lat rows of sequence s
   constexpr int KO = 16;                            // dv <= 4096
   float o[KO];
 #pragma unroll
@@ -153,9 +154,11 @@ __global__ __launch_bounds__(256) void prefill_attn_simt_kernel(
 
 bool launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st) {
   if (act == K_F32) {
+    // the whole context as one block (kb rows per sequence)
+    if (a.k0 != 0 || a.state_in || a.state_out || a.kb < a.max_ctx) return false;
     size_t sh = size_t(a.dn + a.dr + 256) * sizeof(float);
     hipLaunchKernelGGL(prefill_attn_simt_kernel, dim3(a.max_q, a.H, a.S), dim3(256), sh, st, a.H, a.dn,
-                       a.dr, a.dv, a.dc, a.max_ctx, a.cu, a.start, static_cast<const float*>(a.qs),
+                       a.dr, a.dv, a.dc, a.kb, a.cu, a.start, static_cast<const float*>(a.qs),
                        static_cast<const float*>(a.kv), static_cast<const float*>(a.lat),
                        static_cast<float*>(a.out));
     return true;

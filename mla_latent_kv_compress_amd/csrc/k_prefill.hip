@@ -20,6 +20,9 @@
 // every chunk where the operand reads expect it (a load instruction fills one contiguous KiB).
 // The query tiles of one (head, sequence) run back to back on one XCD, heaviest (latest in the
 // chunk, most keys) first, so their key and value reads are shared through that XCD's L2.
+// Long contexts are decompressed in key blocks (positions [k0, k0 + kb)); one launch per block
+// continues the online softmax from the state the previous block saved (the unnormalised output,
+// the running max and the row sum per query and head), and the last one normalises.
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_lds.h"
@@ -84,9 +87,9 @@ __device__ __forceinline__ int load_lds_offset(int k, int wave) {
 
 template <int OUT>
 __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
-    int H, int S, int nqt, int max_ctx, const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
+    int H, int S, int nqt, int k0, int kb, const int32_t* __restrict__ cu, const int32_t* __restrict__ start,
     const uint16_t* __restrict__ qs, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ kpe,
-    typename StoreT<OUT>::type* __restrict__ out) {
+    typename StoreT<OUT>::type* __restrict__ out, const float* __restrict__ state_in, float* __restrict__ state_out) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,15 +106,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
   const int q_begin = cu[s], len = cu[s + 1] - q_begin, st0 = start[s];
   if (qt * kQT >= len) return;                     // the whole work-group leaves together
   const int ctx = st0 + len;
-  const int key_end = st0 + min(len, (qt + 1) * kQT);
-  const int nt = (key_end + kKT - 1) / kKT;
+  const int key_end = st0 + min(len, (qt + 1) * kQT);   // keys the tile's last query sees
+  // This key block: positions [k0, k0 + kb), row t of the buffers holding position k0 + t.
+  const int blk_end = min(key_end, k0 + kb);
+  const int nt = blk_end > k0 ? (blk_end - k0 + kKT - 1) / kKT : 0;
+  const int ctx_rows = min(ctx, k0 + kb) - k0;           // rows of the block inside the context
   const int ql = lane & 31, e = lane >> 5;
   const int qi = qt * kQT + 32 * wave + ql;        // this lane's query (column of S^T)
   const int qpos = st0 + min(qi, len - 1);
   const int wave_qmin = st0 + qt * kQT + 32 * wave;
   const uint32_t row_bytes = uint32_t(H) * 512u;
-  const char* kvc = reinterpret_cast<const char*>(kv) + (long(s) * max_ctx * H + h) * 512;
-  const char* kpec = reinterpret_cast<const char*>(kpe) + long(s) * max_ctx * 128;
+  const char* kvc = reinterpret_cast<const char*>(kv) + (long(s) * kb * H + h) * 512;
+  const char* kpec = reinterpret_cast<const char*>(kpe) + long(s) * kb * 128;
 
   // Query fragments (B operand): Q[query ql][16 st + 8 e .. +7].
   f16x8_t qn[8], qr[4];
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
     char* dst = smem + (j & 1) * kTileBytes;
     const char* kvb = kvc + long(kKT * j) * row_bytes;
     const char* lb = kpec + long(kKT * j) * 128;
-    const int valid = min(kKT, ctx - kKT * j);
+    const int valid = min(kKT, ctx_rows - kKT * j);
     if (valid == kKT) {
 #pragma unroll
       for (int k = 0; k < kLoadsPerWave; ++k)
@@ -176,6 +182,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[vt][j] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  // The state an earlier key block left (the unnormalised output, the running max and the row
+  // sum; the sum goes to the lane of the pair that holds key half 0).
+  if (state_in && qi < len) {
+    const float* sp = state_in + (long(q_begin + qi) * H + h) * 130;
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) o[vt][k] = sp[32 * vt + 8 * (k >> 2) + 4 * e + (k & 3)];
+    m_run = sp[128];
+    l_run = e == 0 ? sp[129] : 0.f;
+  }
 
   issue(0);
   for (int j = 0; j < nt; ++j) {
@@ -184,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
     else wait_vm<0>();
     barrier();                                 // tile j in LDS for every wave
     const char* t = smem + (j & 1) * kTileBytes;
-    const int t0 = kKT * j;
+    const int t0 = k0 + kKT * j;                 // position of the tile's first key
 
     f32x16_t sc[2];
 #pragma unroll
@@ -252,7 +269,17 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (qi < len) {
+  if (qi < len && state_out) {                   // more key blocks follow: pass the state on
+    float* sp = state_out + (long(q_begin + qi) * H + h) * 130;
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sp[32 * vt + 8 * (k >> 2) + 4 * e + (k & 3)] = o[vt][k];
+    if (e == 0) {
+      sp[128] = m_run;
+      sp[129] = l_tot;
+    }
+  } else if (qi < len) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const long row = (long(q_begin + qi) * H + h) * 128;
 #pragma unroll
@@ -267,14 +294,15 @@ bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st) {
   if (a.dn != 128 || a.dr != 64 || a.dv != 128 || a.dc != 512) return false;
   const int nqt = (a.max_q + kQT - 1) / kQT;
   const dim3 grid(unsigned(8L * nqt * ((long(a.H) * a.S + 7) / 8)));
+  if (a.kb <= 0 || a.kb % kKT != 0) return false;
   if (a.out_type == K_BF16)
-    hipLaunchKernelGGL(prefill_attn_fa_kernel<S_BF16>, grid, dim3(256), 0, st, a.H, a.S, nqt, a.max_ctx, a.cu,
+    hipLaunchKernelGGL(prefill_attn_fa_kernel<S_BF16>, grid, dim3(256), 0, st, a.H, a.S, nqt, a.k0, a.kb, a.cu,
                        a.start, static_cast<const uint16_t*>(a.qs), static_cast<const uint16_t*>(a.kv),
-                       static_cast<const uint16_t*>(a.kpe), static_cast<uint16_t*>(a.out));
+                       static_cast<const uint16_t*>(a.kpe), static_cast<uint16_t*>(a.out), a.state_in, a.state_out);
   else
-    hipLaunchKernelGGL(prefill_attn_fa_kernel<S_F32>, grid, dim3(256), 0, st, a.H, a.S, nqt, a.max_ctx, a.cu,
+    hipLaunchKernelGGL(prefill_attn_fa_kernel<S_F32>, grid, dim3(256), 0, st, a.H, a.S, nqt, a.k0, a.kb, a.cu,
                        a.start, static_cast<const uint16_t*>(a.qs), static_cast<const uint16_t*>(a.kv),
-                       static_cast<const uint16_t*>(a.kpe), static_cast<float*>(a.out));
+                       static_cast<const uint16_t*>(a.kpe), static_cast<float*>(a.out), a.state_in, a.state_out);
   return true;
 }
 

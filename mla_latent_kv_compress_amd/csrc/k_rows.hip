@@ -513,22 +513,22 @@ void launch_decode_merge(int B, int H, int dc, int splits, const float* part_o, 
 }
 
 // ------------------------------------------------------------------ prefill gather
-// lat[s][t][:] = cache row of position t of sequence s, t < ctx_s; zero beyond.  bf16 / fp32
-// caches: the stored values.  fp8 cache: the codes' values (exact in bf16), with the token's
-// scale in tscale[s][t] (1 beyond the context), which the decompression applies in fp32.  kpe16
-// (bf16 path) gets the k_pe part (columns [dc, W)) as fp16: the stored value, or scale * code
-// rounded once.
+// lat[s][r][:] = cache row of position k0 + r of sequence s (one key block of kb rows per
+// sequence), zero past the sequence's context.  bf16 / fp32 caches: the stored values.  fp8
+// cache: the codes' values (exact in bf16), with the token's scale in tscale[s][r] (1 past the
+// context), which the decompression applies in fp32.  kpe16 (bf16 path) gets the k_pe part
+// (columns [dc, W)) as fp16: the stored value, or scale * code rounded once.
 template <typename ActT, int CACHE>
-__global__ __launch_bounds__(256) void gather_rows_kernel(int max_ctx, int W, int dc, const int32_t* __restrict__ cu,
+__global__ __launch_bounds__(256) void gather_rows_kernel(int k0, int kb, int W, int dc, const int32_t* __restrict__ cu,
                                                           const int32_t* __restrict__ start,
                                                           const int32_t* __restrict__ bt, int max_blocks,
                                                           const void* __restrict__ cache,
                                                           const float* __restrict__ cache_scale,
                                                           ActT* __restrict__ lat, uint16_t* __restrict__ kpe16,
                                                           float* __restrict__ tscale) {
-  const int s = blockIdx.y, t = blockIdx.x;
+  const int s = blockIdx.y, t = k0 + blockIdx.x;     // position t, row blockIdx.x of the block
   const int ctx = start[s] + (cu[s + 1] - cu[s]);
-  const long row = long(s) * max_ctx + t;
+  const long row = long(s) * kb + blockIdx.x;
   ActT* dst = lat + row * W;
   uint16_t* pe = kpe16 ? kpe16 + row * (W - dc) : nullptr;          // pe[i - dc], i in [dc, W)
   if (t >= ctx) {
@@ -552,12 +552,12 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(int max_ctx, int W, in
   }
 }
 
-void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, int dc, const int32_t* cu,
+void launch_gather_rows(int act, int cache, int S, int k0, int rows, int kb, int W, int dc, const int32_t* cu,
                         const int32_t* start, const int32_t* bt, int max_blocks, const void* cache_data,
                         const float* cache_scale, void* lat, void* kpe16, float* tscale, hipStream_t st) {
-  dim3 grid(max_ctx, S);
-#define MLA_GR(A, C)                                                                                 \
-  hipLaunchKernelGGL((gather_rows_kernel<A, C>), grid, dim3(256), 0, st, max_ctx, W, dc, cu, start, bt, \
+  dim3 grid(rows, S);
+#define MLA_GR(A, C)                                                                                   \
+  hipLaunchKernelGGL((gather_rows_kernel<A, C>), grid, dim3(256), 0, st, k0, kb, W, dc, cu, start, bt, \
                      max_blocks, cache_data, cache_scale, static_cast<A*>(lat), static_cast<uint16_t*>(kpe16), tscale)
   if (act == K_F32) {
     MLA_GR(float, K_F32);

@@ -397,7 +397,7 @@ size_t mla_prefill_workspace_size(const mla_config* cfg, int32_t num_seqs, int32
       max_ctx <= 0)
     return 0;
   PrefillPlan p;
-  plan_prefill(d, path, num_seqs, total_tokens, max_q_len, max_ctx, &p);
+  plan_prefill(d, path, num_seqs, total_tokens, max_q_len, max_ctx, cfg->prefill_key_block, &p);
   return p.bytes;
 }
 
@@ -413,13 +413,13 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
   Path path;
   check_config(cfg, &d, &path);
   PrefillPlan p;
-  plan_prefill(d, path, num_seqs, total_tokens, max_q_len, max_ctx, &p);
+  plan_prefill(d, path, num_seqs, total_tokens, max_q_len, max_ctx, cfg->prefill_key_block, &p);
   if (!workspace || workspace_bytes < p.bytes) return MLA_ERR_WORKSPACE;
   if (path == PATH_BF16 && cfg->cache_dtype == MLA_FP8_E4M3) {
     // the fp8 decompression applies the token scales in the large-tile kernel's epilogue
-    GemmArgs probe = gemm(path, false, K_F16, max_ctx, int(long(d.H) * d.dkv()), d.dc, whole(d.dc), num_seqs,
-                          at(workspace, p.off_lat), d.W(), long(max_ctx) * d.W(), w->kv_b_proj, d.dc, 0,
-                          at(workspace, p.off_kv), long(d.H) * d.dkv(), long(max_ctx) * d.H * d.dkv());
+    GemmArgs probe = gemm(path, false, K_F16, p.kb, int(long(d.H) * d.dkv()), d.dc, whole(d.dc), num_seqs,
+                          at(workspace, p.off_lat), d.W(), long(p.kb) * d.W(), w->kv_b_proj, d.dc, 0,
+                          at(workspace, p.off_kv), long(d.H) * d.dkv(), long(p.kb) * d.H * d.dkv());
     probe.row_scale = reinterpret_cast<const float*>(at(workspace, p.off_tscale));
     if (!launch_gemm_tile_ok(probe)) return MLA_ERR_UNSUPPORTED;
   }
@@ -454,30 +454,41 @@ int mla_prefill(const mla_config* cfg, const mla_weights* w, const void* hidden,
   void* kpe = path == PATH_BF16 ? at(workspace, p.off_kpe) : nullptr;
   const bool fp8 = path == PATH_BF16 && cfg->cache_dtype == MLA_FP8_E4M3;
   float* tscale = fp8 ? reinterpret_cast<float*>(at(workspace, p.off_tscale)) : nullptr;
-  launch_gather_rows(act, kdt(cfg->cache_dtype), S, max_ctx, d.W(), d.dc, cu_seqlens, start_pos, block_table,
-                     max_blocks, cache->data, cache->scale, lat, kpe, tscale, s);
-  // Decompress every context latent: kv[s][t] = kv_b_proj . latent -> per head [k_nope | v]
-  // (fp8 cache: kv_b_proj . codes, times the token's scale in fp32).
   void* kv = at(workspace, p.off_kv);
   const long nkv = long(d.H) * d.dkv();
-  GemmArgs gkv = gemm(path, false, K_F16, max_ctx, int(nkv), d.dc, whole(d.dc), S, lat, d.W(), long(max_ctx) * d.W(),
-                      w->kv_b_proj, d.dc, 0, kv, nkv, long(max_ctx) * nkv);
-  if (fp8) {
-    gkv.row_scale = tscale;
-    gkv.srs = max_ctx;
-  }
-  launch_gemm(gkv, s);
+  const int kb = p.kb;
   PrefillAttnArgs a;
   a.S = S; a.H = d.H; a.dn = d.dn; a.dr = d.dr; a.dv = d.dv; a.dc = d.dc;
   a.max_q = max_q_len; a.max_ctx = max_ctx; a.out_type = kdt(cfg->out_dtype);
   a.cu = cu_seqlens; a.start = start_pos;
   a.qs = qs; a.kv = kv; a.lat = lat; a.kpe = kpe; a.out = out;
+  a.kb = kb;
   if (w->o_proj) {
     // attention output in act dtype to the workspace, then out = o_proj [heads side by side]
     a.out = at(workspace, p.off_attn);
     a.out_type = act;
   }
-  if (!launch_prefill_attn(act, a, s)) return MLA_ERR_UNSUPPORTED;
+  float* state = kb < max_ctx ? reinterpret_cast<float*>(at(workspace, p.off_state)) : nullptr;
+  // Key blocks of kb positions, one after another: gather the block's cached rows, decompress
+  // them (kv[s][t] = kv_b_proj . latent -> per head [k_nope | v]; fp8 cache: kv_b_proj . codes,
+  // times the token's scale in fp32), then attend to them, the running softmax state carried in
+  // `state` from block to block and normalised into the output after the last.
+  for (int k0 = 0; k0 < max_ctx; k0 += kb) {
+    const int rows = max_ctx - k0 < kb ? max_ctx - k0 : kb;
+    launch_gather_rows(act, kdt(cfg->cache_dtype), S, k0, rows, kb, d.W(), d.dc, cu_seqlens, start_pos, block_table,
+                       max_blocks, cache->data, cache->scale, lat, kpe, tscale, s);
+    GemmArgs gkv = gemm(path, false, K_F16, rows, int(nkv), d.dc, whole(d.dc), S, lat, d.W(), long(kb) * d.W(),
+                        w->kv_b_proj, d.dc, 0, kv, nkv, long(kb) * nkv);
+    if (fp8) {
+      gkv.row_scale = tscale;
+      gkv.srs = kb;
+    }
+    launch_gemm(gkv, s);
+    a.k0 = k0;
+    a.state_in = k0 > 0 ? state : nullptr;
+    a.state_out = k0 + kb < max_ctx ? state : nullptr;
+    if (!launch_prefill_attn(act, a, s)) return MLA_ERR_UNSUPPORTED;
+  }
   if (w->o_proj) {
     const long nv = long(d.H) * d.dv;
     launch_gemm(gemm(path, false, kdt(cfg->out_dtype), T, d.D, int(nv), whole(int(nv)), 1, a.out, nv, 0, w->o_proj,

@@ -129,23 +129,32 @@ void launch_merge_splits(int B, int H, int dc, int splits, const uint16_t* part_
 void launch_decode_merge(int B, int H, int dc, int splits, const float* part_o, const float* part_ml,
                          float* otilde, hipStream_t st);
 
-// Prefill: gather each sequence's cached rows [0, ctx) into lat [S][max_ctx][W] (an fp8 cache's
-// codes as their exact values, the token scales into tscale [S][max_ctx]); with kpe16 also their
-// k_pe part (columns [dc, W), dequantised) in fp16 into kpe16 [S][max_ctx][W - dc].
-void launch_gather_rows(int act, int cache, int S, int max_ctx, int W, int dc, const int32_t* cu,
+// Prefill: gather the cached rows of positions [k0, k0 + rows) of each sequence (zeros past its
+// context) into lat [S][kb][W], row t for position k0 + t (an fp8 cache's codes as their exact
+// values, the token scales into tscale [S][kb]); with kpe16 also their k_pe part (columns
+// [dc, W), dequantised) in fp16 into kpe16 [S][kb][W - dc].
+void launch_gather_rows(int act, int cache, int S, int k0, int rows, int kb, int W, int dc, const int32_t* cu,
                         const int32_t* start, const int32_t* bt, int max_blocks,
                         const void* cache_data, const float* cache_scale, void* lat, void* kpe16,
                         float* tscale, hipStream_t st);
 
 // Causal attention of packed chunk queries against decompressed keys / values.
+// Keys and values of positions [k0, k0 + kb) (one key block; row t is position k0 + t).
+// state_in (null for the first block) holds the running softmax state the previous block left,
+// state_out (null for the last block) receives it instead of the output: fp32 [T][H][dv + 2],
+// per (query, head) the unnormalised output, then the running max and the row sum (bf16 path;
+// the fp32 path takes the whole context as one block).
 struct PrefillAttnArgs {
   int S, H, dn, dr, dv, dc, max_q, max_ctx, out_type;
   const int32_t* cu; const int32_t* start;
   const void* qs;            // [T][H][dn+dr], pre-scaled by sigma*log2 e (fp16 on the bf16 path)
-  const void* kv;            // [S][max_ctx][H][dn+dv]  (fp16 on the bf16 path)
-  const void* lat;           // [S][max_ctx][dc+dr] act dtype (k_pe at column dc)
-  const void* kpe;           // [S][max_ctx][dr] fp16 copy of k_pe (bf16 path)
+  const void* kv;            // [S][kb][H][dn+dv]  (fp16 on the bf16 path)
+  const void* lat;           // [S][kb][dc+dr] act dtype (k_pe at column dc)
+  const void* kpe;           // [S][kb][dr] fp16 copy of k_pe (bf16 path)
   void* out;                 // [T][H][dv] out_type
+  int k0 = 0, kb = 0;
+  const float* state_in = nullptr;
+  float* state_out = nullptr;
 };
 // False (nothing launched) when no kernel takes the shape.
 bool launch_prefill_attn(int act, const PrefillAttnArgs& a, hipStream_t st);

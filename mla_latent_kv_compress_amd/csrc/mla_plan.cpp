@@ -48,6 +48,7 @@ int check_config(const mla_config* cfg, Dims* d, Path* path) {
   if (c.act_dtype != MLA_F32 && c.act_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
   if (dtype_size(c.cache_dtype) == 0) return MLA_ERR_INVALID_ARG;
   if (c.out_dtype != MLA_F32 && c.out_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (c.prefill_key_block < 0) return MLA_ERR_INVALID_ARG;
 
   Dims dd;
   dd.D = c.hidden_size; dd.H = c.num_heads; dd.dq = c.q_lora_rank; dd.dc = c.kv_lora_rank;
@@ -193,7 +194,21 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   return MLA_OK;
 }
 
-int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, PrefillPlan* p) {
+static int prefill_key_block(const Dims& d, Path path, int S, int max_ctx, int key_block) {
+  const long whole = rup(max_ctx, 64);
+  if (path != PATH_BF16) return int(whole);
+  long kb = key_block;
+  if (kb <= 0) {
+    // the decompressed keys and values of all sequences (fp16) within 2 GiB
+    const long per_row = long(S) * d.H * d.dkv() * 2;
+    kb = (2L << 30) / per_row / 64 * 64;
+    if (kb < 64) kb = 64;
+  }
+  kb = rup(kb, 64);
+  return int(kb < whole ? kb : whole);
+}
+
+int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, int key_block, PrefillPlan* p) {
   (void)max_q;
   Layout L;
   size_t act = path == PATH_F32 ? 4 : 2;
@@ -202,10 +217,12 @@ int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx,
   p->off_pos = L.take(size_t(T) * 4);
   p->off_slot = L.take(size_t(T) * 8);
   p->off_qs = L.take(size_t(T) * d.H * d.dqk() * act);
-  p->off_lat = L.take(size_t(S) * max_ctx * d.W() * act);
-  p->off_kpe = L.take(size_t(S) * max_ctx * d.dr * 2);
-  p->off_kv = L.take(size_t(S) * max_ctx * d.H * d.dkv() * act);
-  p->off_tscale = L.take(path == PATH_BF16 && d.cache_dt == MLA_FP8_E4M3 ? size_t(S) * max_ctx * 4 : 0);
+  p->kb = prefill_key_block(d, path, S, max_ctx, key_block);
+  p->off_lat = L.take(size_t(S) * p->kb * d.W() * act);
+  p->off_kpe = L.take(size_t(S) * p->kb * d.dr * 2);
+  p->off_kv = L.take(size_t(S) * p->kb * d.H * d.dkv() * act);
+  p->off_tscale = L.take(path == PATH_BF16 && d.cache_dt == MLA_FP8_E4M3 ? size_t(S) * p->kb * 4 : 0);
+  p->off_state = L.take(p->kb < max_ctx ? size_t(T) * d.H * (d.dv + 2) * 4 : 0);
   p->q16 = path == PATH_BF16 && d.dq > 0 && d.dq % 64 == 0 && p->q.direct;
   p->off_wq16 = L.take(p->q16 ? size_t(d.H) * d.dqk() * d.dq * 2 : 0);
   p->off_attn = L.take(size_t(T) * d.H * d.dv * act);

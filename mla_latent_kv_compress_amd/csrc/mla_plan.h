@@ -112,17 +112,21 @@ struct PrefillPlan {
   size_t off_pos;             // int32 [T]
   size_t off_slot;            // int64 [T]
   size_t off_qs;              // [T][H][dqk] scaled, RoPE'd queries (fp32; fp16 on the bf16 path)
-  size_t off_lat;             // act  [S][max_ctx][W] gathered (dequantised) cache rows
-  size_t off_kpe;             // fp16 [S][max_ctx][dr] their k_pe part (bf16 path)
-  size_t off_kv;              // [S][max_ctx][H*dkv] decompressed k_nope | v (fp32; fp16 on the bf16 path)
-  size_t off_tscale;          // fp32 [S][max_ctx] token scales of an fp8 cache (bf16 path)
+  size_t off_lat;             // act  [S][kb][W] gathered (dequantised) cache rows of one key block
+  size_t off_kpe;             // fp16 [S][kb][dr] their k_pe part (bf16 path)
+  size_t off_kv;              // [S][kb][H*dkv] decompressed k_nope | v (fp32; fp16 on the bf16 path)
+  size_t off_tscale;          // fp32 [S][kb] token scales of an fp8 cache (bf16 path)
   size_t off_wq16;            // fp16 copy of q_b_proj (bf16 path with a query LoRA, q16)
   bool q16;                   // bf16 path, dq > 0, dq % 64 == 0: the normed query latent and
                               // q_b_proj enter the q_b projection in fp16
   size_t off_attn;            // act [T][H][dv] attention output before o_proj (weights with o_proj)
+  int kb;                     // key block: positions decompressed at a time (lat, kpe, kv and
+                              // tscale hold kb rows per sequence); >= max_ctx: one block
+  size_t off_state;           // fp32 [T][H][dv + 2] running softmax state between key blocks
   size_t bytes;
 };
-int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, PrefillPlan* p);
+// key_block: mla_config.prefill_key_block (0: the library's choice).
+int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx, int key_block, PrefillPlan* p);
 
 // Per-call argument checks (pointers, sizes); return a status.
 int check_compress_args(const mla_config* cfg, const mla_weights* w, const void* hidden,

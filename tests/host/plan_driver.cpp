@@ -173,7 +173,7 @@ int main(int argc, char** argv) {
     Path p;
     if (check_config(&c, &d, &p) != MLA_OK) return 2;
     PrefillPlan pp;
-    plan_prefill(d, p, std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]), &pp);
+    plan_prefill(d, p, std::atoi(argv[2]), std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]), 0, &pp);
     std::printf("{\"q16\": %s, \"bytes\": %zu}\n", pp.q16 ? "true" : "false", pp.bytes);
     return 0;
   }

@@ -77,6 +77,7 @@ def test_status_strings():
                                       rope_beta_slow=32.0), 1),
     (dict(rope_factor=8.0, rope_original_max_position=4096, rope_beta_fast=32.0, rope_beta_slow=-1.0), 1),
     (dict(rope_mscale=-1.0), 1), (dict(rope_factor=float("inf")), 1),
+    (dict(prefill_key_block=-64), 1),
 ])
 def test_config_validation(bad, code):
     L = api.lib()
@@ -154,6 +155,21 @@ def test_workspace_sizes_and_splits():
         assert 1 <= s <= 64
     c = cfg()
     assert L.mla_decode_num_splits(ctypes.byref(c), 64, 129) * 64 * 2 >= 256   # fills 256 CUs
+
+
+def test_prefill_workspace_bounded_by_the_key_block():
+    """The prefill workspace holds one key block of decompressed keys and values per sequence:
+    with the library's choice it stays near 2 GiB of them however long the context (plus the
+    running softmax state), and an explicit block bounds it further."""
+    L = api.lib()
+    c = cfg()
+    size = lambda cc, ctx: L.mla_prefill_workspace_size(ctypes.byref(cc), 4, 4096, 1024, ctx)
+    whole = size(c, 4096)
+    assert size(c, 8192) > whole                          # two blocks' worth fits under the budget
+    assert size(c, 131072) < 3 * 2 ** 30                  # 128K: blocks, not the whole context
+    assert size(c, 131072) == size(c, 65536)              # bounded by the block, not the context
+    c.prefill_key_block = 1024
+    assert size(c, 131072) < whole
 
 
 def test_decode_split_choice_for_the_workloads():
