@@ -140,6 +140,20 @@ def test_p6_yarn_by_parts_limits():
     assert np.all(fy <= f) and np.all(fy >= f / s)      # between position interpolation and none
 
 
+def test_p6_yarn_ramp_interior_by_hand():
+    """Inside the ramp the frequency is linear in the turn count r: for d = 4 and base 100 the
+    pairs turn at f = 1 and f = 0.1; with an original context of 170 pi, pair 1 makes r = 8.5
+    turns, halfway from beta_slow = 1 to beta_fast = 16 (g = 1/2), so at factor s = 4 it turns
+    at (1/2)(0.1 / 4) + (1/2)(0.1) = 0.0625; with 95 pi it makes 4.75 turns (g = 1/4) and turns
+    at (3/4)(0.1 / 4) + (1/4)(0.1) = 0.04375.  Pair 0 (85 and 47.5 turns, above beta_fast)
+    keeps f = 1.  (A ramp running the other way, or over the pair index, gives other values.)"""
+    kw = dict(factor=4.0, beta_fast=16.0, beta_slow=1.0)
+    np.testing.assert_allclose(oracle.rope_frequencies(4, 100.0, original=170 * math.pi, **kw), [1.0, 0.0625],
+                               rtol=1e-12)
+    np.testing.assert_allclose(oracle.rope_frequencies(4, 100.0, original=95 * math.pi, **kw), [1.0, 0.04375],
+                               rtol=1e-12)
+
+
 def test_p6_yarn_relative_position_and_mscale():
     g = np.random.default_rng(6)
     q, k = g.standard_normal(64), g.standard_normal(64)
