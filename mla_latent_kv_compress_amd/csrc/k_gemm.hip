@@ -180,9 +180,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
 // global->LDS loads, several stages ahead of the MFMAs.  A stage is 64 k of X (MR = 64 or 128
 // rows) and of W.  bf16 rows are 128 bytes with 16-byte chunk c of row r stored at
 // c ^ ((r >> 1) & 7), so the 16 rows of an MFMA operand read fall on distinct banks.  With XF
-// the activation X is fp32 (rows of 256 bytes, chunk c of row r at c ^ (r & 15)) and enters the
-// matrix core as a bf16 pair hi = bf16(x), lo = bf16(x - hi): two products per fragment, so the
-// activation is carried to about 2^-16 of its value instead of bf16's 2^-9.  Rows past M (or N)
+// the activation X is a bf16 pair hi = bf16(x), lo = bf16(x - hi) laid side by side (row m: hi
+// in columns [0, K), lo in [K, 2K)); a stage holds each row's 64-wide hi and lo slices as one
+// 256-byte row (16 chunks: hi 0..7, lo 8..15; chunk c of row r at c ^ (r & 15)), and both enter
+// the matrix core, two products per fragment, so the activation is carried to about 2^-16 of
+// its value instead of bf16's 2^-9 (the pair is formed once, by the producer of X, not by every
+// work-group that reads it).  Rows past M (or N)
 // re-read the last valid row; their outputs are not stored.  Requires K and the K chunk to be
 // multiples of 64.
 namespace {
@@ -216,7 +219,7 @@ __device__ __forceinline__ void sk_barrier() {
 // One skinny problem: Y[z / nsplit] (+ split z % nsplit) = alpha X W^T over the split's K chunk.
 struct SkinnyProb {
   int M, N, K, kchunk, nsplit;
-  const void* X;             // bf16, or fp32 (entering the products as a bf16 hi + lo pair)
+  const void* X;             // bf16, or a bf16 hi + lo pair (XF: row m = [hi (K) | lo (K)])
   long lda, sx;
   const uint16_t* W;
   long ldw, sw;
@@ -253,7 +256,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int b = z / nsplit, sp = z % nsplit;
-  const char* X = reinterpret_cast<const char*>(p.X) + b * p.sx * (XF ? 4 : 2);
+  const char* X = reinterpret_cast<const char*>(p.X) + b * p.sx * 2;
   const uint16_t* W = p.W + b * p.sw;
   typename StoreT<OUT>::type* Y = static_cast<typename StoreT<OUT>::type*>(p.Y) + b * p.sy + sp * p.ssplit;
   const int k0 = sp * kchunk;
@@ -270,8 +273,8 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
     if (q < XK) {
       if constexpr (XF) {
         const int r = 4 * q + (lane >> 4);
-        const int c = (lane & 15) ^ (r & 15);
-        off[j] = uint32_t((long(min(r, M - 1)) * lda + 4 * c) * 4);
+        const int c = (lane & 15) ^ (r & 15);           // hi chunks 0..7, lo chunks 8..15
+        off[j] = uint32_t((long(min(r, M - 1)) * lda + (c < 8 ? 8 * c : K + 8 * (c - 8))) * 2);
       } else {
         const int r = 8 * q + (lane >> 3);
         const int c = (lane & 7) ^ ((r >> 1) & 7);
@@ -290,7 +293,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int q = wave + 4 * j;                       // uniform: q < XK selects X
-      sk_dma16(q < XK ? X + kb * (XF ? 4 : 2) : reinterpret_cast<const char*>(W) + kb * 2, off[j],
+      sk_dma16(q < XK ? X + kb * 2 : reinterpret_cast<const char*>(W) + kb * 2, off[j],
                sk_lds_addr(st + q * 1024));
     }
   };
@@ -334,21 +337,11 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
       [[maybe_unused]] bf16x8_t al[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        if constexpr (XF) {                             // 8 fp32 values: stored chunks of 2 (4kk + g), + 1
+        if constexpr (XF) {                             // hi: stored chunk 4 kk + g, lo: 8 + 4 kk + g
           const char* row = st + arow[t] * kXB;
           const int sw = arow[t] & 15;
-          const float4 x0 = *reinterpret_cast<const float4*>(row + 16 * ((8 * kk + 2 * g) ^ sw));
-          const float4 x1 = *reinterpret_cast<const float4*>(row + 16 * ((8 * kk + 2 * g + 1) ^ sw));
-          const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-          bf16x8v hi, lo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            hi[e] = (__bf16)v[e];                       // round to nearest even
-            lo[e] = (__bf16)(v[e] - (float)hi[e]);
-          }
-          af[t] = __builtin_bit_cast(bf16x8_t, hi);
-          al[t] = __builtin_bit_cast(bf16x8_t, lo);
+          af[t] = *reinterpret_cast<const bf16x8_t*>(row + 16 * ((4 * kk + g) ^ sw));
+          al[t] = *reinterpret_cast<const bf16x8_t*>(row + 16 * ((8 + 4 * kk + g) ^ sw));
         } else {
           af[t] = *reinterpret_cast<const bf16x8_t*>(st + arow[t] * 128 + 16 * ((4 * kk + g) ^ ((arow[t] >> 1) & 7)));
         }
@@ -854,10 +847,9 @@ static void launch_bf16(const GemmArgs& g, hipStream_t st) {
 // The skinny kernel's conditions: TN, M <= 128, K and the chunk in 64-steps, 16-byte rows, and
 // per-operand offsets that fit the 32-bit load offsets.
 static bool skinny_ok(const GemmArgs& g) {
-  const long xs = g.xf32 ? 4 : 2;
   return g.kind == GEMM_BF16 && !g.nn && g.M <= 128 && g.K % 64 == 0 && g.kchunk % 64 == 0 &&
-         g.lda % (16 / xs) == 0 && g.ldw % 8 == 0 && long(g.M) * g.lda * xs < (1L << 32) &&
-         long(g.N) * g.ldw * 2 < (1L << 32);
+         g.lda % 8 == 0 && g.ldw % 8 == 0 && (!g.xpair || g.lda >= 2L * g.K) &&
+         long(g.M) * g.lda * 2 < (1L << 32) && long(g.N) * g.ldw * 2 < (1L << 32);
 }
 
 bool launch_gemm_skinny_ok(const GemmArgs& g) { return skinny_ok(g); }
@@ -899,11 +891,11 @@ template <bool NN, int OUT>
 static void launch_bf16_shape(const GemmArgs& g, hipStream_t st) {
   long tiles_big = long((g.M + 127) / 128) * ((g.N + 127) / 128) * g.batch * g.nsplit;
   if (!NN && skinny_ok(g)) {
-    if (g.xf32) launch_skinny<OUT, true>(g, skinny_prob(g), st);
+    if (g.xpair) launch_skinny<OUT, true>(g, skinny_prob(g), st);
     else launch_skinny<OUT, false>(g, skinny_prob(g), st);
     return;
   }
-  if (g.xf32) return;                               // (callers check skinny_ok first)
+  if (g.xpair) return;                              // (callers check skinny_ok first)
   if (g.M <= 64)
     launch_bf16<64, 128, 64, NN, OUT>(g, st);
   else if (tiles_big >= 256)
@@ -924,7 +916,7 @@ bool launch_q_split_gemm(const GemmArgs& g, float* q_pe, hipStream_t st) {
   SkinnyProb p = skinny_prob(g);
   p.Y2 = q_pe;
   const GemmArgs one = g;
-  if (g.xf32) launch_skinny<kOutQSplit, true>(one, p, st);
+  if (g.xpair) launch_skinny<kOutQSplit, true>(one, p, st);
   else launch_skinny<kOutQSplit, false>(one, p, st);
   return true;
 }

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
 }
 
 bool launch_gemm_tile_ok(const GemmArgs& g) {
-  if (g.kind != GEMM_BF16 || g.nn || g.nsplit != 1 || g.xf32) return false;
+  if (g.kind != GEMM_BF16 || g.nn || g.nsplit != 1 || g.xpair) return false;
   if (g.out != K_BF16 && g.out != K_F16) return false;
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return false;
   if (g.K % kTK != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || g.ldw % 8 != 0 || g.ldc % 8 != 0) return false;

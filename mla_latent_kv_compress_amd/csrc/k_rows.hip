@@ -172,6 +172,29 @@ __device__ __forceinline__ void rmsnorm_row(int t, int T, int n, int nsplit, con
     stf<OutT>(out, long(t) * n + i, row[i] * r * ldf<ActT>(gamma, i));
 }
 
+// The same normalised row stored as a bf16 pair: hi = bf16(y) in out[t][0, n), lo = bf16(y - hi)
+// in out[t][n, 2n) (round to nearest even both), so a bf16 product of hi and of lo carries y to
+// about 2^-16 of its value.
+template <typename ActT>
+__device__ __forceinline__ void rmsnorm_row_pair(int t, int T, int n, int nsplit, const float* __restrict__ acc,
+                                                 const ActT* __restrict__ gamma, uint16_t* __restrict__ out,
+                                                 float eps, float* row, float* red) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const float v = split_sum(acc, nsplit, long(T) * n, long(t) * n + i);
+    row[i] = v;
+    ss += v * v;
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / float(n) + eps);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const float y = row[i] * r * ldf<ActT>(gamma, i);
+    const uint16_t hi = f2bf(y);
+    out[long(t) * 2 * n + i] = hi;
+    out[long(t) * 2 * n + n + i] = f2bf(y - bf2f(hi));
+  }
+}
+
 template <typename ActT, typename OutT>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsplit,
                                                            const float* __restrict__ acc,
@@ -183,14 +206,14 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(int T, int n, int nsp
 }
 
 // Decode: the compress epilogue of the T new tokens (blocks [0, T)) and the RMSNorm of their
-// query latents (blocks [T, 2T), written in fp32: the query projection takes them as a bf16
-// hi + lo pair) in one launch; the two read disjoint partials.
+// query latents (blocks [T, 2T), written as a bf16 hi + lo pair [T][2 nq], which the query
+// projection takes as two products) in one launch; the two read disjoint partials.
 template <typename ActT, int CACHE>
 __global__ __launch_bounds__(256) void decode_rows_kernel(
     int dc, int dr, int T, int nsplit_kv, const float* __restrict__ acc_kv, const ActT* __restrict__ gamma_kv,
     void* __restrict__ cache, float* __restrict__ cache_scale, long num_slots, float eps, RopeParams rp,
     float* __restrict__ rope_tab, const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks,
-    int nq, int nsplit_q, const float* __restrict__ acc_q, const ActT* __restrict__ gamma_q, float* __restrict__ cq) {
+    int nq, int nsplit_q, const float* __restrict__ acc_q, const ActT* __restrict__ gamma_q, uint16_t* __restrict__ cq) {
   extern __shared__ float row[];                    // [max(dc + dr, nq)]
   __shared__ float red[16];
   const int t = blockIdx.x;
@@ -198,7 +221,7 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(
     compress_row<ActT, CACHE>(t, dc, dr, T, nsplit_kv, acc_kv, gamma_kv, nullptr, nullptr, cache, cache_scale,
                               num_slots, eps, rp, rope_tab, ctx, bt, max_blocks, row, red);
   else
-    rmsnorm_row<ActT, float>(t - T, T, nq, nsplit_q, acc_q, gamma_q, cq, eps, row, red);
+    rmsnorm_row_pair<ActT>(t - T, T, nq, nsplit_q, acc_q, gamma_q, cq, eps, row, red);
 }
 
 bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
@@ -211,7 +234,7 @@ bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv
   hipLaunchKernelGGL((decode_rows_kernel<uint16_t, C>), dim3(2 * T), dim3(256), sh, st, dc, dr, T, nsplit_kv, \
                      acc_kv, static_cast<const uint16_t*>(gamma_kv), cache_data, cache_scale, num_slots, eps, \
                      rp, rope_tab, ctx, bt, max_blocks, nq, nsplit_q, acc_q,                        \
-                     static_cast<const uint16_t*>(gamma_q), static_cast<float*>(cq))
+                     static_cast<const uint16_t*>(gamma_q), static_cast<uint16_t*>(cq))
   if (cache == K_BF16)
     MLA_DR(K_BF16);
   else

@@ -117,7 +117,7 @@ void enqueue_query(const Dims& d, Path path, const mla_config* cfg, const mla_we
 
 // Decode front on the bf16 path with a query LoRA: the kv_a and q_a projections in one launch,
 // the compress epilogue and the query-latent RMSNorm in one launch, then q_b.  The normed query
-// latent stays fp32 and enters the q_b products as a bf16 hi + lo pair; with the split epilogue
+// latent leaves the row kernel as a bf16 hi + lo pair and enters the q_b products as two; with the split epilogue
 // (no K split, d_n 128, d_r 64) q_nope leaves scaled in fp32 for the absorb, q_pe in fp32.  Same
 // computation as enqueue_compress + enqueue_query up to rounding; false (nothing enqueued) if the
 // grouped launch does not apply.
@@ -127,14 +127,14 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
                           bool* qsplit, hipStream_t s) {
   *qsplit = false;
   const QueryPlan& q = p.q;
-  if (path != PATH_BF16 || d.dq <= 0 || q.direct || !p.cq_f32) return false;
+  if (path != PATH_BF16 || d.dq <= 0 || q.direct || !p.cq_pair) return false;
   float* acc_kv = reinterpret_cast<float*>(at(ws, p.comp.off_acc));
   float* acc_q = reinterpret_cast<float*>(at(ws, q.off_qa_acc));
-  float* cq = reinterpret_cast<float*>(at(ws, q.off_cq));
+  void* cq = at(ws, q.off_cq);                        // bf16 hi + lo pair [B][2 dq]
   const long nq = long(d.H) * d.dqk();
-  GemmArgs g_b = gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, d.dq, 0, w->q_b_proj, d.dq, 0,
+  GemmArgs g_b = gemm(path, false, K_F32, B, int(nq), d.dq, q.split_b, 1, cq, 2L * d.dq, 0, w->q_b_proj, d.dq, 0,
                       at(ws, q.off_q_acc), nq, 0);
-  g_b.xf32 = true;
+  g_b.xpair = true;
   if (!launch_gemm_skinny_ok(g_b)) return false;
   const GemmArgs g_q = gemm(path, false, K_F32, B, d.dq, d.D, q.split_a, 1, hidden, d.D, 0, w->q_a_proj, d.D, 0,
                             acc_q, d.dq, 0);

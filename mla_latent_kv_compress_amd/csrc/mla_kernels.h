@@ -21,8 +21,9 @@ struct GemmArgs {
   const void* W; long ldw, sw;
   void* Y; long ldc, sy, ssplit;
   float alpha;
-  bool xf32 = false;         // X is fp32 and enters the bf16 products as a hi + lo pair (skinny
-                             // kernel only: launch_gemm_skinny_ok must hold)
+  bool xpair = false;        // X is a bf16 hi + lo pair, row m holding hi in columns [0, K) and
+                             // lo in [K, 2K) (lda counts bf16 values), that enters the products as
+                             // two (skinny kernel only: launch_gemm_skinny_ok must hold)
   bool f16in = false;        // X and W are fp16 (large-tile kernel only)
   const float* row_scale = nullptr;  // large-tile kernel: output row m of batch z times
   long srs = 0;                      // row_scale[z * srs + m]
@@ -37,7 +38,7 @@ bool launch_gemm_tile(const GemmArgs& g, hipStream_t st);
 // Whether the large-tile kernel takes the problem's shape (always so for fp16 operands or a row
 // scale, which only it implements).
 bool launch_gemm_tile_ok(const GemmArgs& g);
-// Whether the skinny (decode-batch) kernel takes this problem; required for xf32.
+// Whether the skinny (decode-batch) kernel takes this problem; required for xpair.
 bool launch_gemm_skinny_ok(const GemmArgs& g);
 // Two independent fp32-output skinny GEMMs in one launch; false (nothing launched) when either
 // does not meet the skinny kernel's conditions.
@@ -72,8 +73,8 @@ void launch_rmsnorm_rows(int act, int T, int n, int nsplit, const float* acc, co
 // dst = fp16 copy of n bf16 values (n a multiple of 8, 16-byte aligned), saturating at +-65504.
 void launch_bf16_to_f16(const void* src, void* dst, long n, hipStream_t st);
 // Decode, bf16 activations: the compress epilogue (positions from the context lengths, RoPE
-// table written) and the query-latent RMSNorm (cq: fp32 [T][nq]) in one launch of 2T blocks;
-// false if unsupported.
+// table written) and the query-latent RMSNorm (cq: bf16 hi + lo pair [T][2 nq]) in one launch
+// of 2T blocks; false if unsupported.
 bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv, const float* acc_kv,
                         const void* gamma_kv, void* cache_data, float* cache_scale, long num_slots, float eps,
                         const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,

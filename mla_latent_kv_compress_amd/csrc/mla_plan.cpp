@@ -155,7 +155,7 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   const SplitK* force = pair.n > 0 ? &pair : nullptr;
   plan_compress(d, path, B, L, &p->comp, force);
   plan_query(d, path, B, L, &p->q, false, force);
-  p->cq_f32 = path == PATH_BF16 && d.dq > 0 && d.dq % 64 == 0;
+  p->cq_pair = path == PATH_BF16 && d.dq > 0 && d.dq % 64 == 0;
   p->off_pos = L.take(size_t(B) * 4);
   p->off_slot = L.take(size_t(B) * 8);
   p->off_qnope = L.take(size_t(B) * d.H * d.dn * act);

@@ -61,8 +61,8 @@ struct QueryPlan {            // q path for T tokens, shared by decode and prefi
   bool direct;                // prefill, bf16 path, no K split: the q projection writes the
                               // scaled fp16 queries straight into their final buffer
   size_t off_qa_acc;          // fp32 [split_a.n][T][dq]          (dq > 0)
-  size_t off_cq;              // [T][dq] normed query latent       (dq > 0): act dtype, or fp32
-                              // (decode, bf16 path) -- room for fp32 either way on the bf16 path
+  size_t off_cq;              // [T][dq] normed query latent       (dq > 0): act dtype, or a bf16
+                              // hi + lo pair [T][2 dq] (decode, bf16 path) -- 4 bytes per value
   size_t off_q_acc;           // fp32 [split_b.n][T][H*dqk]        (!direct)
 };
 
@@ -76,8 +76,9 @@ constexpr int kOrderMax = 2048;
 
 struct DecodePlan {
   int splits;
-  bool cq_f32;                // the grouped decode front applies: fp32 query latent, taken by the
-                              // q_b projection as a bf16 hi + lo pair (bf16 path, dq > 0, dq % 64 == 0)
+  bool cq_pair;                // the grouped decode front applies: the query latent as a bf16 hi + lo
+                              // pair, taken by the q_b projection as two products (bf16 path, dq > 0,
+                              // dq % 64 == 0)
   bool ordered;               // rank the sequences by length before the attention (more than one
                               // round of work-groups on the 64-head kernel, at most 8 splits)
   size_t off_order;           // int32 [B]

@@ -53,7 +53,7 @@ def ctx_blocks(lengths):
 def test_ranking_rule(driver, B, max_len, splits, ranked):
     plan = json.loads(run(driver, "decode", 128, B, ctx_blocks([max_len]), splits))
     assert plan["ordered"] is ranked
-    assert plan["cq_f32"] is True
+    assert plan["cq_pair"] is True
 
 
 def test_auto_splits(driver):
