@@ -44,12 +44,14 @@
  *                                           a multiple of 16, hidden_size and q_lora_rank
  *                                           multiples of 8
  * Precision of the bf16 path: weights, hidden states and the cache are read as stored;
- * products accumulate in fp32.  Decode carries the normed query latent and q_nope in fp32 into
- * their projections (each as a bf16 hi + lo pair), scores the cache with the absorbed query's
+ * products accumulate in fp32.  Decode carries the normed query latent and q_nope to their
+ * projections as bf16 hi + lo pairs (about 16 significant bits), scores the cache with the
+ * absorbed query's
  * latent part in bf16 and its RoPE part in fp16 (the rotary key converted exactly), and weights
  * the latents with bf16 probabilities; each split's softmax state is handed to the merge in fp16
  * under a per-head power-of-two scale (11 significant bits of every entry within 2^-29 of the
- * head's largest).  Prefill rounds the normed query latent, queries, decompressed keys / values
+ * head's largest); the merged latent enters W_UV as a hi + lo pair and the attention output
+ * enters o_proj in bf16.  Prefill rounds the normed query latent, queries, decompressed keys / values
  * and probabilities to fp16 before its MFMAs (q_b_proj enters as an fp16 copy, exact for
  * magnitudes 2^-14 .. 65504; stores to fp16 saturate at +-65504); an fp8 cache enters the
  * decompression as exact code values with the token scale applied in fp32.
