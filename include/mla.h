@@ -46,9 +46,11 @@
  * Precision of the bf16 path: weights, hidden states and the cache are read as stored;
  * products accumulate in fp32.  Decode carries the normed query latent and q_nope to their
  * projections as bf16 hi + lo pairs (about 16 significant bits), scores the cache with the
- * absorbed query's
- * latent part in bf16 and its RoPE part in fp16 (the rotary key converted exactly), and weights
- * the latents with bf16 probabilities; each split's softmax state is handed to the merge in fp16
+ * absorbed query's latent part in bf16 and its RoPE part in fp16 (the rotary key converted
+ * exactly; an fp8 cache's latent codes are scored as stored, in fp8 products against the bf16
+ * query latent as two e4m3 codes per value, hi + lo / 16 with a power-of-two scale per head, 8
+ * significant bits), and weights the latents with bf16 probabilities; each split's softmax
+ * state is handed to the merge in fp16
  * under a per-head power-of-two scale (11 significant bits of every entry within 2^-29 of the
  * head's largest); the merged latent enters W_UV as a hi + lo pair and the attention output
  * enters o_proj in bf16.  Prefill rounds the normed query latent, queries, decompressed keys / values

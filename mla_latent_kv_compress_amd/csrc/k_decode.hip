@@ -47,12 +47,17 @@
 //
 // fp8 cache (e4m3 codes plus one fp32 scale per token): the same kernel with 576-byte rows, so a
 // 32-token stage is 18 KiB of codes plus the stage's 32 scales, and the ring holds 8 stages.  The
-// codes are converted exactly to bf16 at the operand reads (v_cvt_scalef32_pk_bf16_fp8 with scale
-// 1) and the token scale s_t is applied outside the products: score = s_t (code . Qhat), and the
-// value product takes p s_t as its weight (l still sums p).  The score operand is one 128-bit read
-// per lane covering two K steps (K permuted the same way in Qhat); the value operand is one
-// ds_read_b64_tr_b8 (lane i of each 16-lane group: column c0 + i over the 8 rows addressed by
-// lanes 2j, 2j + 1).  Stored chunk of row r, logical chunk c: c ^ ((r >> 2) & 3).
+// token scale s_t is applied outside the products: score = s_t (code . Qhat), and the value
+// product takes p s_t as its weight (l still sums p).  Scores over the latent use the codes as
+// they are, in v_mfma_scale_f32_16x16x128_f8f6f4 (K 128 per product, A: two 128-bit reads per
+// lane, block scale 1) against the query slice as two e4m3 codes per value, hi and lo, with
+// per-head power-of-two block scales 2^e and 2^(e - 4): hi + lo / 16 keeps the 8 significant
+// bits of the bf16 query, and an fp8 product does twice the bf16 work per cycle, so the pair
+// costs the bf16 product's matrix time while the conversion of every key code disappears.  The
+// RoPE part's codes are converted exactly to fp16 for fp16 products, and the value operand (one
+// ds_read_b64_tr_b8: lane i of each 16-lane group gets column c0 + i over the 8 rows addressed
+// by lanes 2j, 2j + 1) exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 1).  Stored chunk of
+// row r, logical chunk c: c ^ ((r >> 2) & 3).
 #include <type_traits>
 
 #include "mla_device.h"
@@ -217,6 +222,24 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+// Four query values x (already divided by their head's power-of-two scale, |x| < 256) as e4m3
+// codes in two words: hi = e4m3(x) and lo = e4m3(16 (x - hi)), both rounded to nearest even
+// (code j in byte j).  hi + lo / 16 carries 8 significant bits, the precision of the bf16 query.
+__device__ __forceinline__ void e4m3_pair4(float x0, float x1, float x2, float x3, int& hi, int& lo) {
+  typedef short s16x2_t __attribute__((ext_vector_type(2)));
+  s16x2_t h = {0, 0}, l = {0, 0};
+  h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x0, x1, 1.0f, false);
+  h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x2, x3, 1.0f, true);
+  hi = __builtin_bit_cast(int, h);
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true);
+  l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, 16.f * (x0 - a[0]), 16.f * (x1 - a[1]), 1.0f, false);
+  l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, 16.f * (x2 - b[0]), 16.f * (x3 - b[1]), 1.0f, true);
+  lo = __builtin_bit_cast(int, l);
+}
+
 }  // namespace
 
 template <bool FP8>
@@ -317,9 +340,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   // every stage) and head half hh (heads [32 hh, 32 hh + 32) of the group).
   // bf16: row 16 mt + li, logical chunk 4 ks + g, stored at (4 ks + g) ^ rsw(li) = 4 (ks ^ y) + x
   // (rsw(16 mt_w + li) = rsw(li)).
-  // fp8: one 16-byte read per lane for K steps 2m, 2m + 1: row 16 mt + li, logical chunk 4m + g,
-  // stored at 4m + (g ^ ((li >> 2) & 3)); bytes 0-7 feed step 2m, bytes 8-15 step 2m + 1, so K
-  // value 8 g + j of step 2m + e is latent column 64m + 16g + 8e + j (Qhat is loaded to match).
+  // fp8: read m (m < 9) is 16 bytes per lane: row 16 mt + li, logical chunk 4m + g, stored at
+  // 4m + (g ^ ((li >> 2) & 3)), i.e. columns 64m + 16g .. +15; reads 2 kb and 2 kb + 1 form the
+  // A operand of latent block kb, read 8 the two fp16 K steps of the RoPE part (byte 8e + j:
+  // column 512 + 16g + 8e + j).  The query is loaded to match.
   const int mt_w = wave & 1, hh = wave >> 1;
   const int sx = g ^ (rsw(li) & 3), sy = rsw(li) >> 2;
   const int s_row = (16 * mt_w + li) * kRowBytes + 16 * (FP8 ? (g ^ ((li >> 2) & 3)) : sx);
@@ -373,20 +397,62 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   };
 
   // ---- score-wave state
-  // Query fragments (B operand of the score product): Qhat[head 32 hh + 16 nt + li][32 ks + 8 g .. +7]
-  // (fp8: the permuted K order above).
+  // Query fragments (B operand of the score product): Qhat[head 32 hh + 16 nt + li][32 ks + 8 g .. +7].
   // Heads past H (a partial last group, e.g. 16 heads in a group of 64) get a zero query: their
   // scores are 0, their sums finite, and nothing of theirs is stored.
-  bf16x8_t qf[2][kKS];
+  // fp8 cache: the latent part enters scaled fp8 products of K 128 (block kb: latent columns
+  // [128 kb, 128 kb + 128)) whose A operand is two of the 16-byte score reads above, so lane
+  // (li, g) holds columns 128 kb + 16 g .. +15 and 128 kb + 64 + 16 g .. +15 of its head, as e4m3
+  // codes hi (qc[..][0], block scale 2^e) and lo (qc[..][1], 2^(e - 4)), e the head's exponent
+  // (its largest |value| below 2^(e + 8)); the RoPE part stays fp16 (qr: columns
+  // 512 + 16 g + 8 i .. +7).
+  bf16x8_t qf[2][FP8 ? 1 : kKS];
+  v8i_t qc[2][FP8 ? 4 : 1][2];
+  f16x8_t qr[2][2];
+  int qsh[2], qsl[2];                                      // hi / lo E8M0 scale bytes per head tile
   if (scorer) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int head = hbase + 32 * hh + 16 * nt + li;
       const uint16_t* q = qhat + (long(b) * H + min(head, H - 1)) * kDW;
+      if constexpr (FP8) {
+        bf16x8_t v[4][4];                                  // [kb][columns +0, +8, +64, +72]
+        float amax = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const int col = FP8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
-        qf[nt][ks] = head < H ? *reinterpret_cast<const bf16x8_t*>(q + col) : bf16x8_t{};
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) {
+            const int col = 128 * kb + 64 * (pt >> 1) + 16 * g + 8 * (pt & 1);
+            v[kb][pt] = head < H ? *reinterpret_cast<const bf16x8_t*>(q + col) : bf16x8_t{};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(float(v[kb][pt][j])));
+          }
+        amax = max_across_rows(amax);                      // over the head's four lanes
+        int ea = 0;
+        frexpf(amax, &ea);                                 // amax < 2^ea
+        const int e = amax > 0.f ? max(ea - 8, -119) : 0;
+        const float inv = __uint_as_float(uint32_t(127 - e) << 23);   // 2^-e
+        qsh[nt] = 127 + e;
+        qsl[nt] = 123 + e;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              int hi, lo;
+              e4m3_pair4(inv * float(v[kb][pt][4 * w]), inv * float(v[kb][pt][4 * w + 1]),
+                         inv * float(v[kb][pt][4 * w + 2]), inv * float(v[kb][pt][4 * w + 3]), hi, lo);
+              qc[nt][kb][0][2 * pt + w] = hi;
+              qc[nt][kb][1][2 * pt + w] = lo;
+            }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          qr[nt][i] = head < H ? *reinterpret_cast<const f16x8_t*>(q + kDC + 16 * g + 8 * i) : f16x8_t{};
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+          qf[nt][ks] = head < H ? *reinterpret_cast<const bf16x8_t*>(q + 32 * ks + 8 * g) : bf16x8_t{};
       }
     }
   }
@@ -473,31 +539,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       for (int q = 0; q < 2; ++q) s[nt][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (FP8) {
       tsc = *reinterpret_cast<const f32x4_t*>(st + Gm::kScaleOff + 4 * (16 * mt_w + 4 * g));
-      constexpr int kR = 3, kM = kKS / 2;
+      // Reads m = 0 .. 7 pair up into the A operands of the four latent blocks (read 2 kb, then
+      // 2 kb + 1); read 8 is the RoPE part.  Reads run two ahead of use.
+      constexpr int kR = 4, kL = 2, kM = kKS / 2;
       uint4 raw[kR];
 #pragma unroll
-      for (int j = 0; j < kR - 1; ++j) raw[j] = score_raw(st, j);
+      for (int j = 0; j < kL; ++j) raw[j] = score_raw(st, j);
 #pragma unroll
       for (int m = 0; m < kM; ++m) {
-        const int mn = m + kR - 1;
+        const int mn = m + kL;
         if (mn < kM) raw[mn % kR] = score_raw(st, mn);
-        const uint4 r = raw[m % kR];
-        if (m < kM - 1) {                                 // latent: bf16 products
-          const bf16x8_t a0 = fp8x8_to_bf16(r.x, r.y), a1 = fp8x8_to_bf16(r.z, r.w);
+        if (m < kM - 1) {                                 // latent: scaled fp8 products, hi and lo
+          if (m & 1) {
+            const uint4 r0 = raw[(m - 1) % kR], r1 = raw[m % kR];
+            const v8i_t a = {int(r0.x), int(r0.y), int(r0.z), int(r0.w), int(r1.x), int(r1.y), int(r1.z), int(r1.w)};
+            const int kb = m >> 1;
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[nt][2 * m], s[nt][0], 0, 0, 0);
+            for (int nt = 0; nt < 2; ++nt)
+              s[nt][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qc[nt][kb][0], s[nt][0], 0, 0, 0, 127, 0, qsh[nt]);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-            s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[nt][2 * m + 1], s[nt][1], 0, 0, 0);
+            for (int nt = 0; nt < 2; ++nt)
+              s[nt][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qc[nt][kb][1], s[nt][1], 0, 0, 0, 127, 0, qsl[nt]);
+          }
         } else {                                          // RoPE part: fp16 products
+          const uint4 r = raw[m % kR];
           const f16x8_t a0 = fp8x8_to_f16(r.x, r.y), a1 = fp8x8_to_f16(r.z, r.w);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
-            s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(f16x8_t, qf[nt][2 * m]), s[nt][0], 0, 0, 0);
+            s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qr[nt][0], s[nt][0], 0, 0, 0);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
-            s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(f16x8_t, qf[nt][2 * m + 1]), s[nt][1], 0, 0, 0);
+            s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qr[nt][1], s[nt][1], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
