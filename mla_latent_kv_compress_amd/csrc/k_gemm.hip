@@ -241,7 +241,7 @@ constexpr int kOutQSplit = 7;
 // 4 fp32 rows of 256 bytes), dealt round-robin to the four waves; wave (wm, wn) computes rows
 // MR / 2 wm .. + MR / 2 and columns BN / 2 wn .. + BN / 2.
 template <int OUT, int BN, int MR, bool XF = false>
-__device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, char* ring) {
+__device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, int rank, char* ring) {
   constexpr int kStageB = sk_stage_bytes<BN, MR, XF>();
   constexpr int S = sk_stages<BN, MR, XF>();
   constexpr int XK = MR * (XF ? 256 : 128) / 1024;       // KiBs of the stage that hold X
@@ -286,10 +286,15 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
       off[j] = uint32_t((long(min(n0 + r, N - 1)) * ldw + 8 * c) * 2);
     }
   }
+  // The work-groups of one XCD that share a K chunk read the same X rows; each starts its K loop
+  // at its own step (rot, from its rank among the XCD's work-groups: work-groups are dealt to
+  // the 8 XCDs round-robin) so that they do not request the same L2 lines at the same time.
+  const int rot = rank % max(nk, 1);
   auto issue = [&](int jj) {
     if (jj >= nk) return;
     char* st = ring + (jj % S) * kStageB;
-    const long kb = long(k0 + 64 * jj);
+    const int js = jj + rot < nk ? jj + rot : jj + rot - nk;
+    const long kb = long(k0 + 64 * js);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int q = wave + 4 * j;                       // uniform: q < XK selects X
@@ -386,7 +391,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
 template <int OUT, int BN, int MR, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(SkinnyProb p) {
   __shared__ __attribute__((aligned(1024))) char ring[sk_stages<BN, MR, XF>() * sk_stage_bytes<BN, MR, XF>()];
-  skinny_tile<OUT, BN, MR, XF>(p, blockIdx.x, blockIdx.z, ring);
+  skinny_tile<OUT, BN, MR, XF>(p, blockIdx.x, blockIdx.z, int((blockIdx.x + gridDim.x * blockIdx.z) >> 3), ring);
 }
 
 // Two independent skinny problems in one launch: work-groups [0, tiles0) take p0's tiles,
@@ -397,10 +402,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_pair_kernel(SkinnyProb p0, Sk
   const int id = blockIdx.x;
   if (id < tiles0) {
     const int nx = (p0.N + BN - 1) / BN;
-    skinny_tile<OUT, BN, MR>(p0, id % nx, id / nx, ring);
+    skinny_tile<OUT, BN, MR>(p0, id % nx, id / nx, id >> 3, ring);
   } else {
     const int nx = (p1.N + BN - 1) / BN;
-    skinny_tile<OUT, BN, MR>(p1, (id - tiles0) % nx, (id - tiles0) / nx, ring);
+    skinny_tile<OUT, BN, MR>(p1, (id - tiles0) % nx, (id - tiles0) / nx, id >> 3, ring);
   }
 }
 

@@ -179,19 +179,31 @@ template <typename ActT>
 __device__ __forceinline__ void rmsnorm_row_pair(int t, int T, int n, int nsplit, const float* __restrict__ acc,
                                                  const ActT* __restrict__ gamma, uint16_t* __restrict__ out,
                                                  float eps, float* row, float* red) {
+  // Four values per thread and step (n % 4 == 0), the loads of every split in flight together.
+  const int n4 = n >> 2;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const float v = split_sum(acc, nsplit, long(T) * n, long(t) * n + i);
-    row[i] = v;
-    ss += v * v;
+  for (int i4 = threadIdx.x; i4 < n4; i4 += blockDim.x) {
+    const float4 v = split_sum4(acc, nsplit, long(T) * n, long(t) * n + 4 * i4);
+    *reinterpret_cast<float4*>(&row[4 * i4]) = v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / float(n) + eps);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const float y = row[i] * r * ldf<ActT>(gamma, i);
-    const uint16_t hi = f2bf(y);
-    out[long(t) * 2 * n + i] = hi;
-    out[long(t) * 2 * n + n + i] = f2bf(y - bf2f(hi));
+  uint16_t* hi_row = out + long(t) * 2 * n;
+  for (int i4 = threadIdx.x; i4 < n4; i4 += blockDim.x) {
+    const float4 v = *reinterpret_cast<const float4*>(&row[4 * i4]);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float y0 = x[2 * j] * r * ldf<ActT>(gamma, 4 * i4 + 2 * j);
+      const float y1 = x[2 * j + 1] * r * ldf<ActT>(gamma, 4 * i4 + 2 * j + 1);
+      const uint16_t h0 = f2bf(y0), h1 = f2bf(y1);
+      hw[j] = uint32_t(h0) | (uint32_t(h1) << 16);
+      lw[j] = uint32_t(f2bf(y0 - bf2f(h0))) | (uint32_t(f2bf(y1 - bf2f(h1))) << 16);
+    }
+    *reinterpret_cast<uint2*>(hi_row + 4 * i4) = make_uint2(hw[0], hw[1]);
+    *reinterpret_cast<uint2*>(hi_row + n + 4 * i4) = make_uint2(lw[0], lw[1]);
   }
 }
 
@@ -228,7 +240,8 @@ bool launch_decode_rows(int act, int cache, int T, int dc, int dr, int nsplit_kv
                         const void* gamma_kv, void* cache_data, float* cache_scale, long num_slots, float eps,
                         const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
                         int nq, int nsplit_q, const float* acc_q, const void* gamma_q, void* cq, hipStream_t st) {
-  if (T <= 0 || act != K_BF16 || (cache != K_BF16 && cache != K_FP8) || !ctx || !rope_tab) return false;
+  if (T <= 0 || act != K_BF16 || (cache != K_BF16 && cache != K_FP8) || !ctx || !rope_tab || nq % 4 != 0)
+    return false;
   const size_t sh = size_t(max(dc + dr, nq)) * sizeof(float);
 #define MLA_DR(C)                                                                                     \
   hipLaunchKernelGGL((decode_rows_kernel<uint16_t, C>), dim3(2 * T), dim3(256), sh, st, dc, dr, T, nsplit_kv, \

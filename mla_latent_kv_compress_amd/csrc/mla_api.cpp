@@ -145,7 +145,7 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
   if (!launch_decode_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
                           w->kv_a_norm, cache->data, cache->scale, num_slots, d.eps, d.rope, rope, ctx, bt,
                           max_blocks, d.dq, q.split_a.n, acc_q, w->q_a_norm, cq, s))
-    return false;                                 // (cannot happen: bf16 activations, bf16 / fp8 cache)
+    return false;                                 // (cannot happen: bf16 activations, bf16 / fp8 cache, q_lora_rank % 64 == 0)
   // q_b with the split epilogue (q_nope as fp32 scale q, q_pe fp32, in the q_acc region) when
   // it applies.
   if (q.split_b.n == 1 && d.dn == 128 && d.dr == 64) {
