@@ -602,18 +602,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) pf[ks][nt] = p_frag(pb, ks, nt);
-    if constexpr (FP8) {                                 // codes read two steps ahead of use
-      v2i_t raw[3];
-      raw[0] = val_raw(st, 0, 0);
-      raw[1] = val_raw(st, 0, 1);
+    if constexpr (FP8) {                                 // codes read four steps ahead, converted one ahead
+      v2i_t raw[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) raw[u] = val_raw(st, u >> 2, u & 3);
+      bf16x8_t av[2];
+      av[0] = fp8x8_to_bf16(uint32_t(raw[0][0]), uint32_t(raw[0][1]));
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (u + 2 < 8) raw[(u + 2) % 3] = val_raw(st, (u + 2) >> 2, (u + 2) & 3);
+        if (u + 4 < 8) raw[u + 4] = val_raw(st, (u + 4) >> 2, (u + 4) & 3);
+        if (u + 1 < 8) av[(u + 1) & 1] = fp8x8_to_bf16(uint32_t(raw[u + 1][0]), uint32_t(raw[u + 1][1]));
         const int ks = u >> 2, ct = u & 3;
-        const bf16x8_t av = fp8x8_to_bf16(uint32_t(raw[u % 3][0]), uint32_t(raw[u % 3][1]));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          o[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks][nt], o[ct][nt], 0, 0, 0);
+          o[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u & 1], pf[ks][nt], o[ct][nt], 0, 0, 0);
       }
       return;
     }
