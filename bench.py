@@ -106,7 +106,12 @@ class HipEvents:
 
 
 def smi_snapshot():
-    """Current shader / memory clock and socket power as rocm-smi reports them (None if absent)."""
+    """Current shader / memory clock and socket power as rocm-smi reports them (None if absent).
+
+    Skipped under a profiler: its preloaded library would initialise the GPU in the child
+    process before that child starts rocm-smi."""
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
                            timeout=30)
