@@ -141,6 +141,33 @@ def test_decode_variants(variant):
         assert e <= TOL["bf16"], (b, e)
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_decode_per_head_query_scales(cache):
+    """Heads whose queries differ in magnitude by powers of two: the q_nope rows of head h in
+    q_b_proj are scaled by 2^(h mod 6 - 3), so the absorbed latent queries of neighbouring heads
+    span 2^-3 .. 2^2 of the default (the largest as sharp as the peaked variant).  On the fp8
+    cache every head's latent query enters the fp8 products with its own power-of-two block
+    scale, which a lane-to-head mix-up of those scales would break; on the bf16 cache the same
+    spread checks the bf16 products.  Bars as for every other case."""
+    from mla_latent_kv_compress_amd.workload import to_device
+    log(f"decode per-head query scales ({cache} cache)")
+    layer = Layer(DSV2, "bf16", cache, seed=4)
+    s = layer.shape
+    w = layer.w_host["q_b_proj"].reshape(s.num_heads, s.qk_head_dim, -1).copy()
+    for h in range(s.num_heads):
+        w[h, :s.qk_nope_head_dim] *= np.float32(2.0 ** ((h % 6) - 3))     # exact in bf16
+    layer.w_host["q_b_proj"] = w.reshape(s.num_heads * s.qk_head_dim, -1)
+    layer.w["q_b_proj"] = to_device(layer.w_host["q_b_proj"], "bf16", "cuda")
+    layer.w_struct = api.make_weights(layer.w)
+    lengths = [90, 333]
+    batch = DecodeBatch(layer, wl(s, "bf16", cache, 2), seed=4, lengths=lengths)
+    out = batch.run(num_splits=2).float().cpu().numpy()
+    for b in range(2):
+        e = rel_err(out[b], decode_reference(layer, batch, b, seed=4))
+        log(f"  seq {b} ctx {lengths[b] + 1}: rel err {e:.2e}")
+        assert e <= TOL[cache], (b, e)
+
+
 @pytest.mark.parametrize("shape,B,splits", [
     (DSV2, 40, 4),     # 128 heads x 2 row blocks of 32 = 256 (head, rows) blocks: all 128 columns per work-group
     (DSV2, 20, 4),     # 128 blocks: the columns cut over 2 work-groups
