@@ -242,6 +242,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
       for (int vt = 0; vt < 4; ++vt) o[vt] *= alpha;
       m_run = m_new;
     }
+    // p = 2^(s - m) with the bare v_exp_f32 (arguments at most kLazy; a query with every key
+    // masked so far keeps m = -inf and takes 2^(-inf - 0) = 0 for each key)
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     f16x8_t pf[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_fa_kernel(
         f16x8_t v;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float p = m_run == -INFINITY ? 0.f : exp2f(sc[u][8 * hf + k] - m_run);
+          const float p = __builtin_amdgcn_exp2f(sc[u][8 * hf + k] - m_use);
           l_run += p;
           v[k] = (_Float16)p;
         }
