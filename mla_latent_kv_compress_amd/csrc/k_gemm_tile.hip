@@ -6,12 +6,14 @@
 //
 // One work-group of 8 waves per 256 x 256 output tile; wave w computes rows
 // [128 (w >> 2), +128) x columns [64 (w & 3), +64) as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
-// (128 fp32 accumulators).  X and W tiles (256 rows x 64 K each, 32 KiB) stream through LDS
-// with direct global->LDS loads, double-buffered (128 KiB); 16-byte chunk c of tile row r is
-// stored at c ^ ((r >> 1) & 7), so the operand reads (16 rows x one chunk per 16 lanes) hit
-// distinct banks.  The result goes through the same LDS (chunk XOR (row & 7)) and leaves as
-// whole 16-byte row segments.  Rows of X or W past M or N re-read the last row; their results
-// are not stored.
+// (128 fp32 accumulators), the product formed transposed (C^T = W X^T, W as the A operand) so
+// that a lane's accumulators hold four consecutive output columns of one row.  X and W tiles
+// (256 rows x 64 K each, 32 KiB) stream through LDS with direct global->LDS loads,
+// double-buffered (128 KiB); 16-byte chunk c of tile row r is stored at c ^ ((r >> 1) & 7), so
+// the operand reads (16 rows x one chunk per 16 lanes) hit distinct banks.  The result goes
+// through the same LDS (chunk XOR (row & 7)) as 8-byte writes of four values converted in pairs
+// and leaves as whole 16-byte row segments.  Rows of X or W past M or N re-read the last row;
+// their results are not stored.
 #include "mla_device.h"
 #include "mla_kernels.h"
 #include "mla_lds.h"
@@ -99,40 +101,54 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 2; ++j) {                // C^T: W fragment as A, X fragment as B
           if constexpr (F16IN)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a[i]),
-                                                               __builtin_bit_cast(f16x8_t, b[j]), acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, b[j]),
+                                                               __builtin_bit_cast(f16x8_t, a[i]), acc[i][j], 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
         }
     }
     lds::barrier();                                  // stage ks's buffer free for stage ks + 2
   }
 
   // Result tile through LDS: [256][256] 2-byte values, 16-byte chunk c of row r at c ^ (r & 7).
-  // C layout: lane holds C[8 (k >> 2) + 4 e + (k & 3)][lane & 31] of each 32 x 32 tile.
+  // C^T layout: lane holds C^T[32 j + 8 (k >> 2) + 4 e + (k & 3)][32 i + (lane & 31)] of each
+  // 32 x 32 tile, i.e. output row m = 128 wm + 32 i + (lane & 31) and, for k = 4 kg .. 4 kg + 3,
+  // four consecutive columns n = 64 wn + 32 j + 8 kg + 4 e .. + 3: one 8-byte LDS write each.
   uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
-  float rs[4][16];
+  float rs[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int m = 128 * wm + 32 * i + 8 * (k >> 2) + 4 * e + (k & 3);
-      rs[i][k] = row_scale ? alpha * row_scale[z * srs + min(m0 + m, M - 1)] : alpha;
+  for (int i = 0; i < 4; ++i) {
+    const int m = 128 * wm + 32 * i + (lane & 31);
+    rs[i] = row_scale ? alpha * row_scale[z * srs + min(m0 + m, M - 1)] : alpha;
+  }
+  auto cvt2 = [](float x, float y) {                 // two values, round to nearest even
+    if constexpr (OUT == S_BF16) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t v = {(__bf16)x, (__bf16)y};
+      return __builtin_bit_cast(uint32_t, v);
+    } else {                                         // fp16, saturating at +-65504
+      typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+      const f16x2_t v = {(_Float16)fminf(fmaxf(x, -65504.0f), 65504.0f),
+                         (_Float16)fminf(fmaxf(y, -65504.0f), 65504.0f)};
+      return __builtin_bit_cast(uint32_t, v);
     }
+  };
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int m = 128 * wm + 32 * i + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = 64 * wn + 32 * j + (lane & 31);
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int m = 128 * wm + 32 * i + 8 * (k >> 2) + 4 * e + (k & 3);
-        const float v = rs[i][k] * acc[i][j][k];
-        ct[m * kTN + 8 * ((n >> 3) ^ (m & 7)) + (n & 7)] = OUT == S_BF16 ? f2bf(v) : f2h_sat(v);
+      for (int kg = 0; kg < 4; ++kg) {
+        const int n = 64 * wn + 32 * j + 8 * kg + 4 * e;
+        const f32x16_t& c = acc[i][j];
+        const uint2 v = make_uint2(cvt2(rs[i] * c[4 * kg], rs[i] * c[4 * kg + 1]),
+                                   cvt2(rs[i] * c[4 * kg + 2], rs[i] * c[4 * kg + 3]));
+        *reinterpret_cast<uint2*>(ct + m * kTN + 8 * ((n >> 3) ^ (m & 7)) + (n & 7)) = v;
       }
-    }
+  }
   lds::barrier();
 #pragma unroll 4
   for (int it = 0; it < kTM * kTN / 8 / 512; ++it) {
