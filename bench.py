@@ -138,37 +138,45 @@ def gpu_info(torch):
 
 
 def stream_bandwidth(torch, nbytes=4 << 30, reps=5):
-    """Read bandwidth of the library's plain stream-read kernel over `nbytes` (more than the caches
-    hold, read after a sweep of another buffer), and a torch device copy (read + write)."""
+    """Read bandwidth over `nbytes` (more than the caches hold, read after a sweep of another
+    buffer) of the library's fastest read (non-temporal direct loads into LDS, the reference), of
+    its plain read into registers, and of a torch device copy (read + write)."""
     from mla_latent_kv_compress_amd import api
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     flush = Flusher(torch)
     dst.copy_(src)
-    api.stream_read(src, sink)
+    api.stream_read(src, sink, 1)
+    api.stream_read(src, sink, 0)
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    cp, rd = [], []
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    cp, rd, rd0 = [], [], []
     for _ in range(reps):
         flush()
         e[0].record()
-        api.stream_read(src, sink)
+        api.stream_read(src, sink, 1)
         e[1].record()
         flush()
         e[2].record()
-        dst.copy_(src)
+        api.stream_read(src, sink, 0)
         e[3].record()
+        flush()
+        e[4].record()
+        dst.copy_(src)
+        e[5].record()
         torch.cuda.synchronize()
         rd.append(e[0].elapsed_time(e[1]))
-        cp.append(e[2].elapsed_time(e[3]))
+        rd0.append(e[2].elapsed_time(e[3]))
+        cp.append(e[4].elapsed_time(e[5]))
     del src, dst, sink, flush
     torch.cuda.empty_cache()
-    rd.sort()
-    cp.sort()
-    return {"read_gbps": nbytes / (rd[len(rd) // 2] * 1e-3) / 1e9, "copy_gbps": 2 * nbytes / (cp[len(cp) // 2] * 1e-3) / 1e9,
-            "bytes": nbytes, "method": "mla_stream_read (read only) and torch device copy (read + write), "
-                                       "median of 5, each after a 1 GiB read sweep"}
+    med = lambda v: sorted(v)[len(v) // 2]
+    return {"read_gbps": nbytes / (med(rd) * 1e-3) / 1e9, "plain_read_gbps": nbytes / (med(rd0) * 1e-3) / 1e9,
+            "copy_gbps": 2 * nbytes / (med(cp) * 1e-3) / 1e9, "bytes": nbytes,
+            "method": "mla_stream_read mode 1 (non-temporal direct loads into LDS: read_gbps, the reference) and "
+                      "mode 0 (plain loads into registers: plain_read_gbps), torch device copy (read + write); "
+                      "median of 5, each after a 1 GiB read sweep"}
 
 
 class Flusher:
@@ -181,7 +189,7 @@ class Flusher:
         self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def __call__(self):
-        self.api.stream_read(self.buf, self.sink)
+        self.api.stream_read(self.buf, self.sink, 0)
 
 
 def workload_work(wl, ctx):

@@ -257,14 +257,17 @@ int mla_fp8_e4m3_encode(const float *x, uint8_t *codes, int64_t n, void *stream)
 int mla_fp8_e4m3_decode(const uint8_t *codes, float *x, int64_t n, void *stream);
 
 /* ---------------------------------------------------------------------------------------
- * mla_stream_read: a measurement reference, not part of the method.  Reads `bytes` (a multiple
- * of 16) from device memory at `src` (16-byte aligned) once, coalesced, and discards them
- * (`sink`: 4 device bytes the kernel may write), so the kernel's duration gives the read
- * bandwidth this GPU reaches for a plain sequential stream; the attention's algorithmic
- * bandwidth is quoted against it beside the published peak.  Asynchronous on `stream`.
- * Returns MLA_ERR_INVALID_ARG for a misaligned or null argument.
+ * mla_stream_read: a measurement aid, not part of the method.  Reads `bytes` (a multiple of 16,
+ * below 4 TiB) from device memory at `src` (16-byte aligned) once, coalesced, and discards them
+ * (`sink`: 4 device bytes the kernel may write).  mode 0: plain loads into registers, a read
+ * sweep that leaves the caches holding clean lines of `src` (used to evict a workload's data
+ * between timed steps).  mode 1: non-temporal direct loads into LDS, the fastest read pattern
+ * measured on this GPU, so the kernel's duration gives the read bandwidth a streaming kernel
+ * can reach; the attention's algorithmic bandwidth is quoted against it beside the published
+ * peak.  Asynchronous on `stream`.  Returns MLA_ERR_INVALID_ARG for a misaligned or null
+ * argument or another mode.
  */
-int mla_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int mla_stream_read(const void *src, size_t bytes, uint32_t *sink, int mode, void *stream);
 
 /* Static text for a status code. */
 const char *mla_status_string(int status);

@@ -62,7 +62,7 @@ SIGNATURES = {
     "mla_fp8_e4m3_decode": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _vp]),
     "mla_decode_noalloc": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                           _i32, _vp, _vp]),
-    "mla_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _vp]),
+    "mla_stream_read": (ctypes.c_int, [_vp, _sz, _vp, ctypes.c_int, _vp]),
     "mla_prefill_workspace_size": (_sz, [_P(MlaConfig), _i32, _i32, _i32, _i32]),
     "mla_prefill": (ctypes.c_int, [_P(MlaConfig), _P(MlaWeights), _vp, _vp, _vp, _vp, _i32, _P(MlaCache), _i32,
                                    _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
@@ -242,7 +242,9 @@ def prefill(cfg, weights, hidden, cu_seqlens, start_pos, block_table, cache, max
     return out
 
 
-def stream_read(src, sink, stream=None):
-    """mla_stream_read: read all of `src` (a contiguous device tensor) once and discard it."""
-    _check(lib().mla_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
-           "mla_stream_read")
+def stream_read(src, sink, mode=0, stream=None):
+    """mla_stream_read: read all of `src` (a contiguous device tensor) once and discard it; mode 0
+    plain cached loads (a cache sweep), mode 1 the non-temporal direct-to-LDS read (the bandwidth
+    reference)."""
+    _check(lib().mla_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), int(mode),
+                                 _stream(stream)), "mla_stream_read")

@@ -157,6 +157,9 @@ __device__ __forceinline__ float sum_across_rows(float v) {
 }
 
 using lds::dma16;
+__device__ __forceinline__ void dma16nt(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
 using lds::dma4;
 using lds::wait_vm;
 __device__ __forceinline__ void lds_barrier() { lds::barrier(); }
@@ -313,17 +316,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     constexpr int kCode = FP8 ? kLoads - 1 : kLoads;      // code loads every wave issues
     if (valid == kStage) {
 #pragma unroll
-      for (int k = 0; k < kCode; ++k) dma16(src, full_off[k], lds_addr(dst + (4 * k + wave) * 1024));
+      for (int k = 0; k < kCode; ++k) dma16nt(src, full_off[k], lds_addr(dst + (4 * k + wave) * 1024));
     } else {
       int ln = lane;
       asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int k = 0; k < kCode; ++k)
-        dma16(src, stage_offset<FP8>(k, wave, ln, valid), lds_addr(dst + (4 * k + wave) * 1024));
+        dma16nt(src, stage_offset<FP8>(k, wave, ln, valid), lds_addr(dst + (4 * k + wave) * 1024));
     }
     if constexpr (FP8) {
       if (wave < 2) {
-        dma16(src, valid == kStage ? full_off[kLoads - 1] : stage_offset<FP8>(kLoads - 1, wave, lane, valid),
+        dma16nt(src, valid == kStage ? full_off[kLoads - 1] : stage_offset<FP8>(kLoads - 1, wave, lane, valid),
               lds_addr(dst + (4 * (kLoads - 1) + wave) * 1024));
       } else {
         const char* ssrc = reinterpret_cast<const char*>(cache_scale) + (page * kPage + kStage * half) * 4;

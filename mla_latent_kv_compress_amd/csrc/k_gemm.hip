@@ -201,6 +201,9 @@ template <int BN, int MR = 64, bool XF = false> constexpr int sk_stages() {
 __device__ __forceinline__ void sk_dma16(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
+__device__ __forceinline__ void sk_dma16nt(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
 __device__ __forceinline__ uint32_t sk_lds_addr(const void* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
@@ -298,8 +301,8 @@ __device__ __forceinline__ void skinny_tile(const SkinnyProb& p, int nx, int z, 
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int q = wave + 4 * j;                       // uniform: q < XK selects X
-      sk_dma16(q < XK ? X + kb * 2 : reinterpret_cast<const char*>(W) + kb * 2, off[j],
-               sk_lds_addr(st + q * 1024));
+      if (q < XK) sk_dma16(X + kb * 2, off[j], sk_lds_addr(st + q * 1024));
+      else sk_dma16nt(reinterpret_cast<const char*>(W) + kb * 2, off[j], sk_lds_addr(st + q * 1024));
     }
   };
   auto wait_for = [&](int jj) {                         // stage jj landed (this wave's part)

@@ -182,12 +182,13 @@ int mla_fp8_e4m3_decode(const uint8_t* codes, float* x, int64_t n, void* stream)
   return finish();
 }
 
-int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
-  if (bytes % 16 != 0 || (bytes > 0 && (!src || !sink)) || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+int mla_stream_read(const void* src, size_t bytes, uint32_t* sink, int mode, void* stream) {
+  if (bytes % 16 != 0 || (bytes > 0 && (!src || !sink)) || (reinterpret_cast<uintptr_t>(src) & 15) != 0 ||
+      (mode != 0 && mode != 1) || bytes >= (size_t(1) << 42))
     return MLA_ERR_INVALID_ARG;
   if (bytes == 0) return MLA_OK;
   (void)hipGetLastError();
-  launch_stream_read(src, long(bytes / 16), sink, static_cast<hipStream_t>(stream));
+  launch_stream_read(src, long(bytes / 16), sink, mode, static_cast<hipStream_t>(stream));
   return finish();
 }
 

@@ -167,7 +167,9 @@ bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st);
 void launch_fp8_codec(bool encode, const void* in, void* out, long n, hipStream_t st);
 // out[i] = sum over the nsplit slices of acc ([nsplit][n] fp32), stored fp32 or bf16 per out_type.
 void launch_sum_splits(int out_type, long n, int nsplit, const float* acc, void* out, hipStream_t st);
-// Reads n16 16-byte words and discards them (a reference for the achievable read bandwidth).
-void launch_stream_read(const void* p, long n16, uint32_t* sink, hipStream_t st);
+// Reads n16 16-byte words and discards them: mode 0 with plain loads into registers (a read
+// sweep that leaves clean lines in the caches), mode 1 with non-temporal direct loads into LDS
+// (the fastest read pattern measured: the reference for the achievable read bandwidth).
+void launch_stream_read(const void* p, long n16, uint32_t* sink, int mode, hipStream_t st);
 
 }  // namespace mla

@@ -129,11 +129,14 @@ def test_argument_validation_returns_before_any_launch():
                                  1 << 30, None) == 1
     assert L.mla_compress_append(ctypes.byref(c), ctypes.byref(w), one, one, one, ctypes.byref(cache), 0, None,
                                  0, None) == 0
-    # stream-read reference: byte count not a multiple of 16, misaligned or null source; 0 bytes no-op
-    assert L.mla_stream_read(one, 24, one, None) == 1
-    assert L.mla_stream_read(ctypes.c_void_p(8), 32, one, None) == 1
-    assert L.mla_stream_read(None, 32, one, None) == 1
-    assert L.mla_stream_read(None, 0, None, None) == 0
+    # stream read: byte count not a multiple of 16, misaligned or null source, unknown mode;
+    # 0 bytes no-op
+    assert L.mla_stream_read(one, 24, one, 0, None) == 1
+    assert L.mla_stream_read(ctypes.c_void_p(8), 32, one, 1, None) == 1
+    assert L.mla_stream_read(None, 32, one, 0, None) == 1
+    assert L.mla_stream_read(one, 32, one, 2, None) == 1
+    assert L.mla_stream_read(one, 32, one, -1, None) == 1
+    assert L.mla_stream_read(None, 0, None, 1, None) == 0
     # prefill: max_ctx beyond the block table, chunk longer than the context
     assert L.mla_prefill(ctypes.byref(c), ctypes.byref(w), one, one, one, one, 2, ctypes.byref(cache), 1, 64, 64,
                          129, one, 1 << 40, one, None) == 1

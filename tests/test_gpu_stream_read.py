@@ -1,4 +1,4 @@
-"""The stream-read reference kernel (a measurement aid): it must read every 16-byte word once.
+"""The stream-read kernels (a measurement aid, both modes): each must read every 16-byte word once.
 
 The kernel XORs the 32-bit words each lane reads and stores the result only when it equals one
 fixed value, so a buffer of zeros with that value in a single word makes the lane that read the
@@ -14,8 +14,9 @@ pytestmark = pytest.mark.gpu
 MAGIC = 0x9E3779B9
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("n16", [1, 7, 1024 * 256, 4 * 1024 * 256 + 5, 3_000_001])
-def test_every_word_is_read(n16):
+def test_every_word_is_read(n16, mode):
     buf = torch.zeros(n16 * 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     magic = MAGIC - (1 << 32)                       # the same bits as a signed int32
@@ -23,11 +24,11 @@ def test_every_word_is_read(n16):
         buf.zero_()
         buf[w] = magic
         sink.zero_()
-        api.stream_read(buf, sink)
+        api.stream_read(buf, sink, mode)
         torch.cuda.synchronize()
         assert int(sink.item()) == magic, (n16, w)
     buf.zero_()
     sink.zero_()
-    api.stream_read(buf, sink)
+    api.stream_read(buf, sink, mode)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
