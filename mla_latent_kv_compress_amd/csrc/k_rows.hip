@@ -641,6 +641,33 @@ void launch_sum_splits(int out_type, long n, int nsplit, const float* acc, void*
                        static_cast<float*>(out));
 }
 
+// The query projection's K-split partials acc [nsplit][T][H][192] summed once (split order) into
+// the layout of the projection's split epilogue: q_nope32 [T][H][128] = alpha q_nope and
+// q_pe32 [T][H][64] = q_pe (fp32), so the absorb reads each query once.  Four values per thread.
+__global__ __launch_bounds__(256) void q_split_sum_kernel(long n4, int nsplit, const float* __restrict__ acc,
+                                                          long stride, float alpha, float* __restrict__ q_nope32,
+                                                          float* __restrict__ q_pe32) {
+  for (long i4 = long(blockIdx.x) * 256 + threadIdx.x; i4 < n4; i4 += long(gridDim.x) * 256) {
+    const long i = 4 * i4;                                    // element of [T][H][192]
+    const float4 v = split_sum4(acc, nsplit, stride, i);
+    const long th = i / 192;
+    const int c = int(i - th * 192);                          // a multiple of 4: never straddles 128
+    if (c < 128)
+      *reinterpret_cast<float4*>(q_nope32 + th * 128 + c) = make_float4(alpha * v.x, alpha * v.y, alpha * v.z, alpha * v.w);
+    else
+      *reinterpret_cast<float4*>(q_pe32 + th * 64 + c - 128) = v;
+  }
+}
+
+void launch_q_split_sum(int T, int H, int nsplit, const float* acc, float alpha, float* q_nope32, float* q_pe32,
+                        hipStream_t st) {
+  const long n4 = long(T) * H * 192 / 4;
+  if (n4 <= 0) return;
+  const long blocks = std::min<long>((n4 + 255) / 256, 1024);
+  hipLaunchKernelGGL(q_split_sum_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, n4, nsplit, acc,
+                     long(T) * H * 192, alpha, q_nope32, q_pe32);
+}
+
 // ------------------------------------------------------------------ stream-read reference
 // Reads n16 16-byte words once (grid-stride, four loads in flight per lane) and keeps only an
 // XOR of them, so the kernel's time is that of reading the bytes from memory.

@@ -299,6 +299,16 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   const float* qn32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)) : nullptr;
   const float* qpe32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc) + size_t(B) * d.H * d.dn * 4)
                               : nullptr;
+  if (!qsplit && path == PATH_BF16 && d.dn == 128 && d.dr == 64 && d.dc == 512) {
+    // The query arrives as K-split partials: sum them once into the split epilogue's layout, in
+    // the attention partials' region (dead until the attention, which runs after the absorb;
+    // B H (dc 2 B) >= B H 192 4 B for any split count)
+    float* qn = reinterpret_cast<float*>(at(workspace, p.off_part_o));
+    float* qp = qn + size_t(B) * d.H * d.dn;
+    launch_q_split_sum(B, d.H, p.q.split_b.n, qacc, qscale, qn, qp, s);
+    qn32 = qn;
+    qpe32 = qp;
+  }
   if (!(path == PATH_BF16 && launch_absorb_rope(B, d.H, d.dn, d.dr, d.dc, d.dv, p.q.split_b.n, qacc, rope, qscale,
                                                 w->kv_b_proj, qhat, s, qn32, qpe32))) {
     if (qsplit) return MLA_ERR_UNSUPPORTED;       // (cannot happen: both need dn 128, dr 64, dc 512)

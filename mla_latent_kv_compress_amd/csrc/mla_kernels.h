@@ -165,6 +165,10 @@ bool launch_prefill_attn_fa(const PrefillAttnArgs& a, hipStream_t st);
 
 // Elementwise e4m3fn codec of the fp8 cache: encode fp32 -> codes, or decode codes -> fp32.
 void launch_fp8_codec(bool encode, const void* in, void* out, long n, hipStream_t st);
+// Decode query (nope 128, rope 64): the projection's partials acc [nsplit][T][H][192] summed into
+// q_nope32 [T][H][128] = alpha q_nope and q_pe32 [T][H][64] (fp32; the absorb's split input).
+void launch_q_split_sum(int T, int H, int nsplit, const float* acc, float alpha, float* q_nope32, float* q_pe32,
+                        hipStream_t st);
 // out[i] = sum over the nsplit slices of acc ([nsplit][n] fp32), stored fp32 or bf16 per out_type.
 void launch_sum_splits(int out_type, long n, int nsplit, const float* acc, void* out, hipStream_t st);
 // Reads n16 16-byte words and discards them: mode 0 with plain loads into registers (a read
