@@ -173,10 +173,13 @@ def test_decode_per_head_query_scales(cache):
     (DSV2, 20, 4),     # 128 blocks: the columns cut over 2 work-groups
     (LITE, 5, 4),      # 16 blocks: the columns cut over 4 work-groups
     (DSV2, 32, 0),     # the library's own choice for 32 sequences of 128 heads: 4 splits
+    (LITE, 40, 8),     # eight splits (merged by a first kernel, then projected), 16 heads x 2 row blocks
+    (DSV2, 20, 8),     # the same with 128 heads
 ])
 def test_four_split_merge(shape, B, splits):
-    """The merge + W_UV kernel's four-split instance in each of its three column forms, and the
-    automatic split count at B = 32 (which picks four)."""
+    """The merge + W_UV kernel's four-split instance in each of its three column forms, the
+    automatic split count at B = 32 (which picks four), and eight splits (merged by a first kernel;
+    many of these short sequences leave some splits empty)."""
     lengths = [int(x) for x in np.random.default_rng(13).integers(0, 260, B)]
     if splits == 0:
         lengths[1] = 700          # a block table of 11 pages: room for 4 splits of whole stages
