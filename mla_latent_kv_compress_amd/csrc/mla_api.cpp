@@ -127,6 +127,21 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
                           bool* qsplit, hipStream_t s) {
   *qsplit = false;
   const QueryPlan& q = p.q;
+  if (p.hidden_pair && !q.direct) {
+    // No query LoRA: the query projection (q_b_proj holds it) and kv_a in one launch, then the
+    // compress epilogue; the query partials are summed before the absorb
+    const long nq = long(d.H) * d.dqk();
+    const GemmArgs g_q = gemm(path, false, K_F32, B, int(nq), d.D, q.split_b, 1, hidden, d.D, 0, w->q_b_proj, d.D, 0,
+                              at(ws, q.off_q_acc), nq, 0);
+    float* acc_kv = reinterpret_cast<float*>(at(ws, p.comp.off_acc));
+    const GemmArgs g_kv = gemm(path, false, K_F32, B, d.W(), d.D, p.comp.split, 1, hidden, d.D, 0, w->kv_a_proj,
+                               d.D, 0, acc_kv, d.W(), 0);
+    if (!launch_gemm_pair(g_q, g_kv, s)) return false;
+    launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
+                         w->kv_a_norm, nullptr, nullptr, cache->data, cache->scale,
+                         long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.rope, rope, ctx, bt, max_blocks, s);
+    return true;
+  }
   if (path != PATH_BF16 || d.dq <= 0 || q.direct || !p.cq_pair) return false;
   float* acc_kv = reinterpret_cast<float*>(at(ws, p.comp.off_acc));
   float* acc_q = reinterpret_cast<float*>(at(ws, q.off_qa_acc));

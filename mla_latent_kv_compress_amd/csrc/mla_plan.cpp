@@ -116,10 +116,10 @@ static void plan_query(const Dims& d, Path path, long T, Layout& L, QueryPlan* q
     q->off_qa_acc = L.take(size_t(q->split_a.n) * T * d.dq * 4);
     q->off_cq = L.take(size_t(T) * d.dq * 4);
     q->split_b = gemm_splitk(T, nq, d.dq, 64, 64);
-  } else {
+  } else {                     // the query projection reads the hidden state: force_a applies to it
     q->split_a = SplitK{1, 32};
     q->off_qa_acc = q->off_cq = 0;
-    q->split_b = gemm_splitk(T, nq, d.D, 64, 64);
+    q->split_b = force_a ? *force_a : gemm_splitk(T, nq, d.D, 64, 64);
   }
   q->direct = allow_direct && path == PATH_BF16 && q->split_b.n == 1;
   q->off_q_acc = q->direct ? 0 : L.take(size_t(q->split_b.n) * T * nq * 4);
@@ -152,10 +152,12 @@ int plan_decode(const Dims& d, Path path, int B, int max_blocks, int splits, Dec
   // LoRA): one K split for both, with the pair's tile shape.
   SplitK pair{0, 0};
   if (path == PATH_BF16 && d.dq > 0) pair = pair_splitk(B, d.dq, d.W(), d.D);
+  else if (path == PATH_BF16) pair = pair_splitk(B, long(d.H) * d.dqk(), d.W(), d.D);
   const SplitK* force = pair.n > 0 ? &pair : nullptr;
   plan_compress(d, path, B, L, &p->comp, force);
   plan_query(d, path, B, L, &p->q, false, force);
   p->cq_pair = path == PATH_BF16 && d.dq > 0 && d.dq % 64 == 0;
+  p->hidden_pair = path == PATH_BF16 && d.dq == 0 && pair.n > 0;
   p->off_pos = L.take(size_t(B) * 4);
   p->off_slot = L.take(size_t(B) * 8);
   p->off_qnope = L.take(size_t(B) * d.H * d.dn * act);

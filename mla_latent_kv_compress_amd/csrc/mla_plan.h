@@ -79,6 +79,9 @@ struct DecodePlan {
   bool cq_pair;                // the grouped decode front applies: the query latent as a bf16 hi + lo
                               // pair, taken by the q_b projection as two products (bf16 path, dq > 0,
                               // dq % 64 == 0)
+  bool hidden_pair;           // no query LoRA (bf16 path, B <= 128): the direct query projection
+                              // and kv_a, both reading the hidden state, run in one launch with
+                              // one K split
   bool ordered;               // rank the sequences by length before the attention (more than one
                               // round of work-groups on the 64-head kernel, at most 8 splits)
   size_t off_order;           // int32 [B]

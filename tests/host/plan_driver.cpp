@@ -162,8 +162,9 @@ int main(int argc, char** argv) {
     if (check_config(&c, &d, &p) != MLA_OK) return 2;
     DecodePlan dp;
     plan_decode(d, p, std::atoi(argv[3]), std::atoi(argv[4]), std::atoi(argv[5]), &dp);
-    std::printf("{\"splits\": %d, \"ordered\": %s, \"cq_pair\": %s, \"bytes\": %zu}\n", dp.splits,
-                dp.ordered ? "true" : "false", dp.cq_pair ? "true" : "false", dp.bytes);
+    std::printf("{\"splits\": %d, \"ordered\": %s, \"cq_pair\": %s, \"hidden_pair\": %s, \"bytes\": %zu}\n",
+                dp.splits, dp.ordered ? "true" : "false", dp.cq_pair ? "true" : "false",
+                dp.hidden_pair ? "true" : "false", dp.bytes);
     return 0;
   }
   if (argc == 6 && !std::strcmp(argv[1], "prefill")) {

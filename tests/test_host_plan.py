@@ -54,6 +54,7 @@ def test_ranking_rule(driver, B, max_len, splits, ranked):
     plan = json.loads(run(driver, "decode", 128, B, ctx_blocks([max_len]), splits))
     assert plan["ordered"] is ranked
     assert plan["cq_pair"] is True
+    assert plan["hidden_pair"] is False              # (a query LoRA: the grouped front instead)
 
 
 def test_auto_splits(driver):
