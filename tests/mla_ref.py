@@ -32,6 +32,34 @@ def history_rows(layer, seq, length, seed=0, chunk=16384):
     return out
 
 
+def decode_rows_and_queries(layer, batch, seq, seed=0):
+    """The oracle's stored rows of sequence `seq` after its decode token is appended, and that
+    token's queries (the first steps of oracle.decode_one)."""
+    d, W = oracle_dims(layer.shape), oracle_weights(layer)
+    L = int(batch.hist[seq])
+    x = batch.x_host[seq].astype(np.float64)
+    new_row, _, _ = oracle.cache_rows(d, W, x[None, :], np.array([L]), layer.cache_dtype)
+    rows = np.concatenate([history_rows(layer, seq, L, seed), new_row], axis=0)
+    q_nope, q_pe = oracle.queries(d, W, x[None, :], np.array([L]))
+    return rows, q_nope[0], q_pe[0]
+
+
+def absorbed_all_heads(layer, rows, q_nope, q_pe):
+    """All heads of one decode token in the weight-absorbed form, fp64, the heads batched into
+    three matrix products (oracle.attend_absorbed computes the same head by head, too slowly for
+    131072 rows): Q^h = [W_UK^h^T q_nope^h | q_pe^h], p^h = softmax(sigma Q^h . rows),
+    o^h = W_UV^h (p^h . rows[:, :d_c]).  A test checks it against the explicit oracle on sampled
+    heads before using it."""
+    d, W = oracle_dims(layer.shape), oracle_weights(layer)
+    dc = d.kv_lora_rank
+    blk = W["kv_b_proj"].reshape(d.heads, d.qk_nope + d.v_head, dc)
+    w_uk, w_uv = blk[:, : d.qk_nope], blk[:, d.qk_nope:]                # [H, d_n, d_c], [H, d_v, d_c]
+    q_hat = np.concatenate([np.einsum("hn,hnc->hc", q_nope, w_uk), q_pe], axis=1)   # [H, d_c + d_r]
+    p = oracle.softmax(d.sigma * (q_hat @ rows.T), axis=1)                # [H, n]
+    o_lat = p @ rows[:, :dc]                                             # [H, d_c]
+    return np.einsum("hvc,hc->hv", w_uv, o_lat)
+
+
 def decode_reference(layer, batch, seq, heads=None, seed=0, hist_rows=None):
     d, W = oracle_dims(layer.shape), oracle_weights(layer)
     L = int(batch.hist[seq])

@@ -2,8 +2,10 @@
 
 Each decode workload runs over its whole batch and paged cache at its real shape with the split
 count the bench uses (seed 0, eager launch, fp32 output); the oracle then recomputes a seeded
-sample of sequences one at a time (all heads, or a fixed head subset where one sequence's
-explicit form would take minutes on the host) and every other output is checked to be finite.
+sample of sequences one at a time (all heads; at long contexts the explicit form on a fixed head
+subset, whose explicit form over every head would take minutes on the host, and every head in
+the weight-absorbed fp64 form, checked against the explicit one on that subset first) and every
+other output is checked to be finite.
 The mixed fp8 workload's chunked prefill (4 prompts x 4096 tokens in chunks of 1024) is checked
 on sampled rows of every chunk; the oracle chains the chunks itself, each chunk's stored rows
 becoming the next one's prior context.
@@ -16,7 +18,8 @@ import oracle
 from mla_latent_kv_compress_amd import api, inputs
 from mla_latent_kv_compress_amd.configs import WORKLOADS
 from mla_latent_kv_compress_amd.workload import DecodeBatch, Layer, PrefillBatch
-from mla_ref import TOL, decode_reference, oracle_dims, oracle_weights, rel_err
+from mla_ref import (TOL, absorbed_all_heads, decode_reference, decode_rows_and_queries, oracle_dims, oracle_weights,
+                     rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +41,8 @@ def picks(batch, count, seed=99):
 @pytest.mark.parametrize("name,count,heads", [
     ("lite_bf16", 3, None),
     ("dsv2_bf16", 2, None),
-    ("dsv2_128k", 1, [0, 61, 127]),
-    ("dsv2_mixed_fp8", 1, [0, 61, 127]),
+    ("dsv2_128k", 4, [0, 61, 127]),
+    ("dsv2_mixed_fp8", 3, [0, 61, 127]),
 ])
 def test_fullsize_decode(name, count, heads):
     wl = WORKLOADS[name]
@@ -53,12 +56,25 @@ def test_fullsize_decode(name, count, heads):
     out = batch.run(num_splits=splits, workspace=ws).float().cpu().numpy()
     assert np.isfinite(out).all()
     bar = TOL["fp8" if wl.cache_dtype == "fp8" else wl.act_dtype]
+    d, W = oracle_dims(layer.shape), oracle_weights(layer)
     for b in picks(batch, count):
-        ref = decode_reference(layer, batch, b, heads=heads)
-        got = out[b] if heads is None else out[b][heads]
-        e = rel_err(got, ref)
-        log(f"  seq {b} ctx {int(batch.ctx[b])}: rel err {e:.2e}")
+        if heads is None:
+            ref = decode_reference(layer, batch, b)
+            e = rel_err(out[b], ref)
+            log(f"  seq {b} ctx {int(batch.ctx[b])}: rel err {e:.2e}")
+            assert e <= bar, (name, b, e)
+            continue
+        # Long contexts: the explicit oracle on the sampled heads, and every head against the
+        # absorbed form, itself checked against the explicit oracle on those heads first
+        rows, q_nope, q_pe = decode_rows_and_queries(layer, batch, b)
+        ref = oracle.attend_explicit(d, W, q_nope[None], q_pe[None], rows, heads=heads)[0]
+        ref_all = absorbed_all_heads(layer, rows, q_nope, q_pe)
+        assert rel_err(ref_all[heads], ref) <= 1e-9, (name, b)
+        e = rel_err(out[b][heads], ref)
+        e_all = rel_err(out[b], ref_all)
+        log(f"  seq {b} ctx {int(batch.ctx[b])}: rel err {e:.2e} (heads {heads}), {e_all:.2e} (all heads)")
         assert e <= bar, (name, b, e)
+        assert e_all <= bar, (name, b, e_all)
 
 
 @pytest.mark.timeout(900)

@@ -373,3 +373,27 @@ def test_fp8_store_scale():
     assert np.max(rel) <= 2.0 ** -4 * 1.0001       # at most half a step of the top binade
     z_vals, z_codes, z_scale = oracle.fp8_store(np.zeros((1, 576)))
     assert z_scale[0] == 1.0 and np.all(z_codes == 0) and np.all(z_vals == 0)
+
+
+def test_batched_absorbed_reference_matches_explicit():
+    """The full-size decode tests' all-heads reference (the absorbed form with the heads batched,
+    tests/mla_ref.py) equals the explicit oracle on random rows and queries (tiny and Lite shapes,
+    every head)."""
+    from mla_latent_kv_compress_amd import inputs
+    from mla_latent_kv_compress_amd.configs import LITE, TINY
+    from mla_ref import absorbed_all_heads, oracle_dims, oracle_weights, rel_err
+
+    class _Layer:
+        pass
+
+    for shape, act in ((TINY, "f32"), (LITE, "bf16")):
+        layer = _Layer()
+        layer.shape, layer.act = shape, act
+        layer.w_host = inputs.make_weights(shape, act, 3)
+        d, W = oracle_dims(shape), oracle_weights(layer)
+        g = np.random.default_rng(1)
+        rows = g.standard_normal((300, d.row_width))
+        qn, qp = g.standard_normal((d.heads, d.qk_nope)), g.standard_normal((d.heads, d.qk_rope))
+        got = absorbed_all_heads(layer, rows, qn, qp)
+        ref = oracle.attend_explicit(d, W, qn[None], qp[None], rows)[0]
+        assert rel_err(got, ref) < 1e-12
