@@ -44,6 +44,30 @@ __device__ __forceinline__ float4 split_sum4(const float* __restrict__ acc, int 
   return v;
 }
 
+// ------------------------------------------------------------------ query partial sum (decode)
+struct QSumArgs {
+  long n4 = 0;                 // (T H 192) / 4; 0: nothing to do
+  int nsplit = 1;
+  const float* acc = nullptr;
+  long stride = 0;             // T H 192
+  float alpha = 1.f;
+  float* q_nope32 = nullptr;
+  float* q_pe32 = nullptr;
+};
+__device__ __forceinline__ void q_split_sum_part(const QSumArgs& q, long part, long parts) {
+  for (long i4 = part * 256 + threadIdx.x; i4 < q.n4; i4 += parts * 256) {
+    const long i = 4 * i4;                                    // element of [T][H][192]
+    const float4 v = split_sum4(q.acc, q.nsplit, q.stride, i);
+    const long th = i / 192;
+    const int c = int(i - th * 192);                          // a multiple of 4: never straddles 128
+    if (c < 128)
+      *reinterpret_cast<float4*>(q.q_nope32 + th * 128 + c) =
+          make_float4(q.alpha * v.x, q.alpha * v.y, q.alpha * v.z, q.alpha * v.w);
+    else
+      *reinterpret_cast<float4*>(q.q_pe32 + th * 64 + c - 128) = v;
+  }
+}
+
 // ------------------------------------------------------------------ compress epilogue
 // One block per token.  a = sum of the kv_a partials = [latent (dc) | k_pe (dr)].
 // latent <- latent / sqrt(mean(latent^2) + eps) * gamma;  k_pe <- RoPE(k_pe, pos);
@@ -120,9 +144,13 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(
     int dc, int dr, int T, int nsplit, const float* __restrict__ acc, const ActT* __restrict__ gamma,
     const int32_t* __restrict__ pos, const int64_t* __restrict__ slots, void* __restrict__ cache,
     float* __restrict__ cache_scale, long num_slots, float eps, RopeParams rp, float* __restrict__ rope_tab,
-    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks) {
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks, QSumArgs qs) {
   extern __shared__ float row[];                    // [dc + dr]
   __shared__ float red[16];
+  if (int(blockIdx.x) >= T) {                       // the query partial sum, in the same launch
+    q_split_sum_part(qs, blockIdx.x - T, gridDim.x - T);
+    return;
+  }
   compress_row<ActT, CACHE>(blockIdx.x, dc, dr, T, nsplit, acc, gamma, pos, slots, cache, cache_scale, num_slots,
                             eps, rp, rope_tab, ctx, bt, max_blocks, row, red);
 }
@@ -131,13 +159,26 @@ void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit,
                           const void* gamma, const int32_t* pos, const int64_t* slots,
                           void* cache_data, float* cache_scale, long num_slots, float eps,
                           const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
-                          hipStream_t st) {
+                          hipStream_t st, int qsplit_n, const float* q_acc, int H, float alpha, float* q_nope32,
+                          float* q_pe32) {
   if (T <= 0) return;
   size_t sh = size_t(dc + dr) * sizeof(float);
+  QSumArgs qs;
+  long qblocks = 0;
+  if (q_acc) {
+    qs.n4 = long(T) * H * 192 / 4;
+    qs.nsplit = qsplit_n;
+    qs.acc = q_acc;
+    qs.stride = long(T) * H * 192;
+    qs.alpha = alpha;
+    qs.q_nope32 = q_nope32;
+    qs.q_pe32 = q_pe32;
+    qblocks = std::min<long>((qs.n4 + 255) / 256, 1024);
+  }
 #define MLA_CR(A, C)                                                                          \
-  hipLaunchKernelGGL((compress_rows_kernel<A, C>), dim3(T), dim3(256), sh, st, dc, dr, T, nsplit, \
+  hipLaunchKernelGGL((compress_rows_kernel<A, C>), dim3(unsigned(T + qblocks)), dim3(256), sh, st, dc, dr, T, nsplit, \
                      acc, static_cast<const A*>(gamma), pos, slots, cache_data, cache_scale,      \
-                     num_slots, eps, rp, rope_tab, ctx, bt, max_blocks)
+                     num_slots, eps, rp, rope_tab, ctx, bt, max_blocks, qs)
   if (act == K_F32) {
     MLA_CR(float, K_F32);
   } else if (cache == K_BF16) {
@@ -643,29 +684,25 @@ void launch_sum_splits(int out_type, long n, int nsplit, const float* acc, void*
 
 // The query projection's K-split partials acc [nsplit][T][H][192] summed once (split order) into
 // the layout of the projection's split epilogue: q_nope32 [T][H][128] = alpha q_nope and
-// q_pe32 [T][H][64] = q_pe (fp32), so the absorb reads each query once.  Four values per thread.
-__global__ __launch_bounds__(256) void q_split_sum_kernel(long n4, int nsplit, const float* __restrict__ acc,
-                                                          long stride, float alpha, float* __restrict__ q_nope32,
-                                                          float* __restrict__ q_pe32) {
-  for (long i4 = long(blockIdx.x) * 256 + threadIdx.x; i4 < n4; i4 += long(gridDim.x) * 256) {
-    const long i = 4 * i4;                                    // element of [T][H][192]
-    const float4 v = split_sum4(acc, nsplit, stride, i);
-    const long th = i / 192;
-    const int c = int(i - th * 192);                          // a multiple of 4: never straddles 128
-    if (c < 128)
-      *reinterpret_cast<float4*>(q_nope32 + th * 128 + c) = make_float4(alpha * v.x, alpha * v.y, alpha * v.z, alpha * v.w);
-    else
-      *reinterpret_cast<float4*>(q_pe32 + th * 64 + c - 128) = v;
-  }
+// q_pe32 [T][H][64] = q_pe (fp32), so the absorb reads each query once.  Four values per thread;
+// `part` of `parts` work-groups take a grid-stride share.
+__global__ __launch_bounds__(256) void q_split_sum_kernel(QSumArgs q) {
+  q_split_sum_part(q, blockIdx.x, gridDim.x);
 }
 
 void launch_q_split_sum(int T, int H, int nsplit, const float* acc, float alpha, float* q_nope32, float* q_pe32,
                         hipStream_t st) {
-  const long n4 = long(T) * H * 192 / 4;
-  if (n4 <= 0) return;
-  const long blocks = std::min<long>((n4 + 255) / 256, 1024);
-  hipLaunchKernelGGL(q_split_sum_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, n4, nsplit, acc,
-                     long(T) * H * 192, alpha, q_nope32, q_pe32);
+  QSumArgs q;
+  q.n4 = long(T) * H * 192 / 4;
+  if (q.n4 <= 0) return;
+  q.nsplit = nsplit;
+  q.acc = acc;
+  q.stride = long(T) * H * 192;
+  q.alpha = alpha;
+  q.q_nope32 = q_nope32;
+  q.q_pe32 = q_pe32;
+  const long blocks = std::min<long>((q.n4 + 255) / 256, 1024);
+  hipLaunchKernelGGL(q_split_sum_kernel, dim3(unsigned(blocks)), dim3(256), 0, st, q);
 }
 
 // ------------------------------------------------------------------ stream-read reference

@@ -124,12 +124,21 @@ void enqueue_query(const Dims& d, Path path, const mla_config* cfg, const mla_we
 bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const mla_weights* w,
                           const void* hidden, const mla_cache* cache, int B, const DecodePlan& p, void* ws,
                           float* rope, const int32_t* ctx, const int32_t* bt, int max_blocks, float qscale,
-                          bool* qsplit, hipStream_t s) {
-  *qsplit = false;
+                          const float** qn32, const float** qpe32, hipStream_t s) {
+  *qn32 = *qpe32 = nullptr;
   const QueryPlan& q = p.q;
   if (p.hidden_pair && !q.direct) {
     // No query LoRA: the query projection (q_b_proj holds it) and kv_a in one launch, then the
-    // compress epilogue; the query partials are summed before the absorb
+    // compress epilogue; where the absorb takes fp32 queries (d_n 128, d_r 64, d_c 512) the same
+    // launch sums the query partials into the split epilogue's layout, in the attention
+    // partials' region (dead until the attention, which runs after the absorb; B H (d_c 2 B) >=
+    // B H 192 4 B for any split count)
+    float* qn = nullptr;
+    float* qp = nullptr;
+    if (d.dn == 128 && d.dr == 64 && d.dc == 512) {
+      qn = reinterpret_cast<float*>(at(ws, p.off_part_o));
+      qp = qn + size_t(B) * d.H * d.dn;
+    }
     const long nq = long(d.H) * d.dqk();
     const GemmArgs g_q = gemm(path, false, K_F32, B, int(nq), d.D, q.split_b, 1, hidden, d.D, 0, w->q_b_proj, d.D, 0,
                               at(ws, q.off_q_acc), nq, 0);
@@ -139,7 +148,11 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
     if (!launch_gemm_pair(g_q, g_kv, s)) return false;
     launch_compress_rows(kdt(cfg->act_dtype), kdt(cfg->cache_dtype), B, d.dc, d.dr, p.comp.split.n, acc_kv,
                          w->kv_a_norm, nullptr, nullptr, cache->data, cache->scale,
-                         long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.rope, rope, ctx, bt, max_blocks, s);
+                         long(cache->num_blocks) * MLA_PAGE_SIZE, d.eps, d.rope, rope, ctx, bt, max_blocks, s,
+                         q.split_b.n, qn ? reinterpret_cast<const float*>(at(ws, q.off_q_acc)) : nullptr, d.H, qscale,
+                         qn, qp);
+    *qn32 = qn;
+    *qpe32 = qp;
     return true;
   }
   if (path != PATH_BF16 || d.dq <= 0 || q.direct || !p.cq_pair) return false;
@@ -169,7 +182,8 @@ bool enqueue_decode_front(const Dims& d, Path path, const mla_config* cfg, const
     GemmArgs g = g_b;
     g.alpha = qscale;
     if (launch_q_split_gemm(g, qpe, s)) {
-      *qsplit = true;
+      *qn32 = reinterpret_cast<const float*>(qn);
+      *qpe32 = qpe;
       return true;
     }
   }
@@ -291,9 +305,12 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   float* rope = reinterpret_cast<float*>(at(workspace, p.off_rope));
   // Scaled queries: sigma * log2(e) folded in, so the kernels use exp2.
   const float qscale = d.sigma * kLog2eHost;
-  bool qsplit = false;
+  // fp32 queries in the split epilogue's layout (q_nope scaled, q_pe), when the front leaves them
+  const float* qn32 = nullptr;
+  const float* qpe32 = nullptr;
   const bool front = enqueue_decode_front(d, path, cfg, w, hidden, cache, B, p, workspace, rope, context_lens,
-                                          block_table, max_blocks, qscale, &qsplit, s);
+                                          block_table, max_blocks, qscale, &qn32, &qpe32, s);
+  const bool qfp32 = qn32 != nullptr;
   if (front) {
     // compress / append and the query projection enqueued by the grouped front
   } else if (path == PATH_BF16) {
@@ -311,10 +328,7 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   const float* qacc = reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc));
   // Absorb: qhat[b][h][0:dc] = q_nope[b][h] . W_UK^h  (W_UK^h = kv_b_proj rows of head h's k_nope),
   // qhat[b][h][dc:] = RoPE(q_pe[b][h]); one kernel on the bf16 path.
-  const float* qn32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc)) : nullptr;
-  const float* qpe32 = qsplit ? reinterpret_cast<const float*>(at(workspace, p.q.off_q_acc) + size_t(B) * d.H * d.dn * 4)
-                              : nullptr;
-  if (!qsplit && path == PATH_BF16 && d.dn == 128 && d.dr == 64 && d.dc == 512) {
+  if (!qfp32 && path == PATH_BF16 && d.dn == 128 && d.dr == 64 && d.dc == 512) {
     // The query arrives as K-split partials: sum them once into the split epilogue's layout, in
     // the attention partials' region (dead until the attention, which runs after the absorb;
     // B H (dc 2 B) >= B H 192 4 B for any split count)
@@ -326,7 +340,7 @@ int mla_decode_timed(const mla_config* cfg, const mla_weights* w, const void* hi
   }
   if (!(path == PATH_BF16 && launch_absorb_rope(B, d.H, d.dn, d.dr, d.dc, d.dv, p.q.split_b.n, qacc, rope, qscale,
                                                 w->kv_b_proj, qhat, s, qn32, qpe32))) {
-    if (qsplit) return MLA_ERR_UNSUPPORTED;       // (cannot happen: both need dn 128, dr 64, dc 512)
+    if (qfp32) return MLA_ERR_UNSUPPORTED;        // (cannot happen: both need dn 128, dr 64, dc 512)
     if (path == PATH_BF16) launch_decode_prep(B, context_lens, block_table, max_blocks, pos, slot, s);
     launch_q_pack(act, act, true, B, d.H, d.dn, d.dr, d.dc, p.q.split_b.n, qacc, pos, qscale, d.rope, qnope, qhat,
                   nullptr, s);

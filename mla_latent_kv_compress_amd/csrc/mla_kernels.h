@@ -52,7 +52,9 @@ void launch_compress_rows(int act, int cache, int T, int dc, int dr, int nsplit,
                           const void* gamma, const int32_t* pos, const int64_t* slots,
                           void* cache_data, float* cache_scale, long num_slots, float eps,
                           const RopeParams& rp, float* rope_tab, const int32_t* ctx, const int32_t* bt, int max_blocks,
-                          hipStream_t st);
+                          hipStream_t st, int qsplit_n = 1, const float* q_acc = nullptr, int H = 0,
+                          float alpha = 1.f, float* q_nope32 = nullptr, float* q_pe32 = nullptr);
+// (With q_acc, the same launch also does launch_q_split_sum's work for T tokens of H heads.)
 // Decode queries on the bf16 path, from the fp32 query projection q ([nsplit][B][H][dn + dr]):
 // qhat[b][h] = [ W_UK^h^T (scale q_nope) (bf16, dc values) | scale RoPE(q_pe) (fp16, dr values) ],
 // q_nope entering the products as a bf16 hi + lo pair; the angles of each token come from
