@@ -31,9 +31,10 @@ struct GemmArgs {
                              // for wide outputs whose K split was planned with it
 };
 void launch_gemm(const GemmArgs& g, hipStream_t st);
-// 256 x 256-tile GEMM (k_gemm_tile.hip) for large TN products with a bf16 or fp16 output and no K
-// split (the prefill's q_b projection and kv_b decompression), bf16 or fp16 operands, optional
-// per-row output scale; false if the problem does not fit.
+// 256 x 256-tile GEMM (k_gemm_tile.hip) for large TN products: bf16 or fp16 outputs without a K
+// split (the prefill's q_b projection and kv_b decompression), or fp32 outputs, also as K-split
+// partials of equal slices for more than 128 rows (the prefill's kv_a and q_a); bf16 or fp16
+// operands, optional per-row output scale; false if the problem does not fit.
 bool launch_gemm_tile(const GemmArgs& g, hipStream_t st);
 // Whether the large-tile kernel takes the problem's shape (always so for fp16 operands or a row
 // scale, which only it implements).

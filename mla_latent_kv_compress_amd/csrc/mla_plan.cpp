@@ -101,6 +101,15 @@ SplitK pair_splitk(long M, long N0, long N1, long K) {
   return SplitK{int(cdiv(K, chunk)), int(chunk)};
 }
 
+SplitK tile_splitk(long M, long N, long K) {
+  const long tiles = cdiv(M, 256) * cdiv(N, 256);
+  const SplitK one{1, int(rup(K, 32))};
+  if (M <= 128 || N <= 0 || tiles >= 192 || K % 64 != 0) return one;   // (N 0: no query LoRA)
+  for (long n = 256 / tiles; n > 1; --n)
+    if (K % (64 * n) == 0 && tiles * n >= 192) return SplitK{int(n), int(K / n)};
+  return one;
+}
+
 int plan_compress(const Dims& d, Path path, long T, Layout& L, CompressPlan* p, const SplitK* force) {
   (void)path;
   p->split = force ? *force : gemm_splitk(T, d.W(), d.D, 64, 64);
@@ -214,8 +223,12 @@ int plan_prefill(const Dims& d, Path path, int S, int T, int max_q, int max_ctx,
   (void)max_q;
   Layout L;
   size_t act = path == PATH_F32 ? 4 : 2;
-  plan_compress(d, path, T, L, &p->comp);
-  plan_query(d, path, T, L, &p->q, true);
+  // kv_a and q_a of a long chunk run on the 256 x 256-tile kernel as fp32 K-split partials
+  const bool tiles = path == PATH_BF16 && T >= 1024;
+  const SplitK kv_split = tile_splitk(T, d.W(), d.D);
+  const SplitK qa_split = d.dq > 0 ? tile_splitk(T, d.dq, d.D) : SplitK{1, 32};
+  plan_compress(d, path, T, L, &p->comp, tiles ? &kv_split : nullptr);
+  plan_query(d, path, T, L, &p->q, true, tiles && d.dq > 0 ? &qa_split : nullptr);
   p->off_pos = L.take(size_t(T) * 4);
   p->off_slot = L.take(size_t(T) * 8);
   p->off_qs = L.take(size_t(T) * d.H * d.dqk() * act);

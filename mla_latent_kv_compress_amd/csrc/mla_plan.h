@@ -49,6 +49,10 @@ SplitK gemm_splitk(long M, long N, long K, int tile_m, int tile_n);
 // together with 96-column tiles, sized so that the pair fills 256 CUs in one round; n = 0 when
 // that launch does not apply (N0 or N1 not a multiple of 96, M > 64, K not a multiple of 64).
 SplitK pair_splitk(long M, long N0, long N1, long K);
+// K split of a prefill-sized fp32-output GEMM (M > 128 rows) for the 256 x 256-tile kernel:
+// equal slices of whole 64-steps, as many as keep the work-groups within one round of 256 while
+// filling at least 192 of them; n = 1 when the tiles alone reach 192 or no such split exists.
+SplitK tile_splitk(long M, long N, long K);
 
 struct CompressPlan {
   SplitK split;

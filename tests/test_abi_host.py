@@ -153,6 +153,9 @@ def test_workspace_sizes_and_splits():
         assert 0 < a < b
         assert L.mla_decode_workspace_size(ctypes.byref(c), 16, 16, 4) > b
         assert L.mla_prefill_workspace_size(ctypes.byref(c), 2, 100, 60, 128) > 0
+        # a long chunk (kv_a and q_a as K-split partials of the 256 x 256-tile kernel; Lite has
+        # no query LoRA)
+        assert L.mla_prefill_workspace_size(ctypes.byref(c), 4, 4096, 1024, 4096) > 0
         assert L.mla_compress_append_workspace_size(ctypes.byref(c), 10) > 0
         s = L.mla_decode_num_splits(ctypes.byref(c), 4, 2049)
         assert 1 <= s <= 64
