@@ -1,5 +1,6 @@
 // Split-K decode attention over a bf16 or fp8 latent cache, 64 heads per work-group
-// (weight-absorbed).
+// (weight-absorbed).  A layer of 32 heads or fewer runs an instance that skips the group's empty
+// head tiles.
 //
 // One work-group of 8 waves per (sequence, split, group of 64 heads), two waves per SIMD with
 // separate roles:
@@ -245,7 +246,7 @@ __device__ __forceinline__ void e4m3_pair4(float x0, float x1, float x2, float x
 
 }  // namespace
 
-template <bool FP8>
+template <bool FP8, int HT>
 __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     int H, int splits, int max_blocks, int by_seq, int nunits, const uint16_t* __restrict__ qhat,
     const void* __restrict__ cache, const float* __restrict__ cache_scale, const int32_t* __restrict__ bt,
@@ -348,6 +349,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
   // A operand of latent block kb, read 8 the two fp16 K steps of the RoPE part (byte 8e + j:
   // column 512 + 16g + 8e + j).  The query is loaded to match.
   const int mt_w = wave & 1, hh = wave >> 1;
+  // Live 16-head tiles of the group: HT of 4.  A narrow layer (H <= 32) fills only head half 0:
+  // the score waves of head half 1 skip their products and operand reads, and so do the value
+  // waves for their second 32-head tile (its P rows are never read).
+  static_assert(HT == 1 || HT == 2 || HT == 4, "live head tiles");
+  constexpr int kSNT = HT >= 2 ? 2 : 1;                    // score head tiles of a live score wave
+  constexpr int kVNT = HT == 4 ? 2 : 1;                    // value head tiles
+  const bool s_live = 32 * hh < 16 * HT;
   const int sx = g ^ (rsw(li) & 3), sy = rsw(li) >> 2;
   const int s_row = (16 * mt_w + li) * kRowBytes + 16 * (FP8 ? (g ^ ((li >> 2) & 3)) : sx);
   const int s_even = s_row + 64 * sy;                      // ks even: + 64 ks
@@ -540,6 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int q = 0; q < 2; ++q) s[nt][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (!s_live) return;                                  // head half past H: scores stay 0
     if constexpr (FP8) {
       tsc = *reinterpret_cast<const f32x4_t*>(st + Gm::kScaleOff + 4 * (16 * mt_w + 4 * g));
       // Reads m = 0 .. 7 pair up into the A operands of the four latent blocks (read 2 kb, then
@@ -558,20 +567,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
             const v8i_t a = {int(r0.x), int(r0.y), int(r0.z), int(r0.w), int(r1.x), int(r1.y), int(r1.z), int(r1.w)};
             const int kb = m >> 1;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < kSNT; ++nt)
               s[nt][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qc[nt][kb][0], s[nt][0], 0, 0, 0, 127, 0, qsh[nt]);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < kSNT; ++nt)
               s[nt][1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qc[nt][kb][1], s[nt][1], 0, 0, 0, 127, 0, qsl[nt]);
           }
         } else {                                          // RoPE part: fp16 products
           const uint4 r = raw[m % kR];
           const f16x8_t a0 = fp8x8_to_f16(r.x, r.y), a1 = fp8x8_to_f16(r.z, r.w);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < kSNT; ++nt)
             s[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qr[nt][0], s[nt][0], 0, 0, 0);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < kSNT; ++nt)
             s[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qr[nt][1], s[nt][1], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -587,12 +596,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       if (kn < kKS) a[kn % kScoreRing] = score_a(st, kn);
       if (ks < kDC / 32) {                       // latent: bf16 products
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < kSNT; ++nt)
           s[nt][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks % kScoreRing], qf[nt][ks], s[nt][ks & 1], 0, 0, 0);
       } else {                                   // RoPE part: the key converted to fp16, fp16 products
         const f16x8_t ah = bf16x8_to_f16(a[ks % kScoreRing]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < kSNT; ++nt)
           s[nt][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, __builtin_bit_cast(f16x8_t, qf[nt][ks]), s[nt][ks & 1], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);        // keep the source order: reads stay ahead of use
@@ -604,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) pf[ks][nt] = p_frag(pb, ks, nt);
+      for (int nt = 0; nt < kVNT; ++nt) pf[ks][nt] = p_frag(pb, ks, nt);
     if constexpr (FP8) {                                 // codes read four steps ahead, converted one ahead
       v2i_t raw[8];
 #pragma unroll
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
         if (u + 1 < 8) av[(u + 1) & 1] = fp8x8_to_bf16(uint32_t(raw[u + 1][0]), uint32_t(raw[u + 1][1]));
         const int ks = u >> 2, ct = u & 3;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < kVNT; ++nt)
           o[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u & 1], pf[ks][nt], o[ct][nt], 0, 0, 0);
       }
       return;
@@ -629,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_attn_latent_kernel(
       if (u + 1 < 8) av[(u + 1) & 1] = val_a(st, (u + 1) >> 2, (u + 1) & 3);
       const int ks = u >> 2, ct = u & 3;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kVNT; ++nt)
         o[ct][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[u & 1], pf[ks][nt], o[ct][nt], 0, 0, 0);
     }
   };
@@ -838,7 +847,14 @@ bool launch_decode_attn_v2(int cache_type, const DecodeAttnArgs& a, hipStream_t 
     hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(1024), 0, st, a.B, a.ctx, a.order);
     order = a.order;
   }
-  const auto kern = cache_type == K_FP8 ? decode_attn_latent_kernel<true> : decode_attn_latent_kernel<false>;
+  // A layer of at most 32 heads fills one group partly: its instance skips the empty head tiles.
+  auto pick = [&](auto fp8) {
+    constexpr bool F = decltype(fp8)::value;
+    return a.H <= 16 ? decode_attn_latent_kernel<F, 1>
+         : a.H <= 32 ? decode_attn_latent_kernel<F, 2>
+                     : decode_attn_latent_kernel<F, 4>;
+  };
+  const auto kern = cache_type == K_FP8 ? pick(std::true_type()) : pick(std::false_type());
   hipLaunchKernelGGL(kern, dim3(unsigned(grid)), dim3(kThreads), 0, st, a.H, a.splits, a.max_blocks, by_seq,
                      int(nunits), static_cast<const uint16_t*>(a.qhat), a.cache, a.cache_scale, a.block_table, a.ctx, order,
                      static_cast<uint16_t*>(a.part_o), a.part_ml);

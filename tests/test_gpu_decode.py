@@ -99,6 +99,10 @@ CASES = {
     "lite_bf16": (LITE, "bf16", "bf16", [1, 127, 450]),
     "lite_fp8": (LITE, "bf16", "fp8", [5, 200]),
     "dsv2_fp8_long": (DSV2, "bf16", "fp8", [31, 1000, 2047]),
+    # 32 and 48 heads: the narrow instance with two live head tiles, and a partial 64-head group
+    "lite32_bf16": (dataclasses.replace(LITE, num_heads=32), "bf16", "bf16", [2, 97, 333]),
+    "lite32_fp8": (dataclasses.replace(LITE, num_heads=32), "bf16", "fp8", [40, 255]),
+    "lite48_bf16": (dataclasses.replace(LITE, num_heads=48), "bf16", "bf16", [9, 190]),
 }
 
 
