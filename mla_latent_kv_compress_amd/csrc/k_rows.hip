@@ -1,6 +1,7 @@
 // Row-wise kernels of the MLA path: cache-row epilogue of the KV compression, the query
 // RMSNorm and packing, index preparation, the split-K merge and the prefill gather.
 #include <algorithm>
+#include <type_traits>
 
 #include "mla_device.h"
 #include "mla_kernels.h"
@@ -671,8 +672,55 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(long n, int nsplit, con
   }
 }
 
+// The same sum, four values per thread, with every split's loads requested before the first add
+// (a loop over a run-time split count would wait for each load in turn); splits added in order.
+template <typename OutT, int MAXS>
+__global__ __launch_bounds__(256) void sum_splits4_kernel(long n4, int nsplit, const float4* __restrict__ acc,
+                                                          OutT* __restrict__ out) {
+  for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n4; i += long(gridDim.x) * 256) {
+    float4 v[MAXS];
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s)
+      if (s < nsplit) v[s] = acc[long(s) * n4 + i];
+    float4 t = v[0];
+#pragma unroll
+    for (int s = 1; s < MAXS; ++s)
+      if (s < nsplit) {
+        t.x += v[s].x;
+        t.y += v[s].y;
+        t.z += v[s].z;
+        t.w += v[s].w;
+      }
+    if constexpr (std::is_same<OutT, float>::value) {
+      reinterpret_cast<float4*>(out)[i] = t;
+    } else {
+      reinterpret_cast<uint2*>(out)[i] = make_uint2(uint32_t(f2bf(t.x)) | (uint32_t(f2bf(t.y)) << 16),
+                                                    uint32_t(f2bf(t.z)) | (uint32_t(f2bf(t.w)) << 16));
+    }
+  }
+}
+
 void launch_sum_splits(int out_type, long n, int nsplit, const float* acc, void* out, hipStream_t st) {
   if (n <= 0) return;
+  const uintptr_t oal = out_type == K_BF16 ? 7 : 15;   // one 8- or 16-byte store per thread
+  if (n % 4 == 0 && nsplit >= 1 && nsplit <= 16 && (reinterpret_cast<uintptr_t>(acc) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(out) & oal) == 0) {
+    const long n4 = n / 4;
+    const long blocks = std::min<long>((n4 + 255) / 256, 2048);
+    const float4* a4 = reinterpret_cast<const float4*>(acc);
+#define MLA_SS4(MAXS)                                                                                 \
+    if (out_type == K_BF16)                                                                           \
+      hipLaunchKernelGGL((sum_splits4_kernel<uint16_t, MAXS>), dim3(unsigned(blocks)), dim3(256), 0, st, n4,     \
+                         nsplit, a4, static_cast<uint16_t*>(out));                                    \
+    else                                                                                              \
+      hipLaunchKernelGGL((sum_splits4_kernel<float, MAXS>), dim3(unsigned(blocks)), dim3(256), 0, st, n4, nsplit, \
+                         a4, static_cast<float*>(out))
+    if (nsplit <= 4) { MLA_SS4(4); }
+    else if (nsplit <= 8) { MLA_SS4(8); }
+    else { MLA_SS4(16); }
+#undef MLA_SS4
+    return;
+  }
   const long blocks = std::min<long>((n + 255) / 256, 2048);
   if (out_type == K_BF16)
     hipLaunchKernelGGL(sum_splits_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(256), 0, st, n, nsplit, acc,
