@@ -121,6 +121,22 @@ def test_decode_matches_oracle(case, splits):
         assert e <= TOL[cache if cache == "fp8" else act], (b, e)
 
 
+@pytest.mark.parametrize("heads,splits", [(16, 16), (32, 8), (32, 20)])
+def test_narrow_heads_many_splits(heads, splits):
+    """The narrow-head instances (one or two live 16-head tiles) with more splits than stages:
+    short contexts leave most splits empty, and above four splits the merge runs first."""
+    shape = dataclasses.replace(LITE, num_heads=heads)
+    lengths = [1, 70, 300]
+    log(f"narrow heads {heads}, splits {splits}")
+    layer = Layer(shape, "bf16", "bf16", seed=7)
+    batch = DecodeBatch(layer, wl(shape, "bf16", "bf16", len(lengths)), seed=7, lengths=lengths)
+    out = batch.run(num_splits=splits).float().cpu().numpy()
+    for b in range(len(lengths)):
+        e = rel_err(out[b], decode_reference(layer, batch, b, seed=7))
+        log(f"  seq {b} ctx {lengths[b] + 1}: rel err {e:.2e}")
+        assert e <= TOL["bf16"], (b, e)
+
+
 @pytest.mark.parametrize("B", [100, 140])
 def test_decode_large_batches(B):
     """100 sequences: the decode projections run as 128-row weight-streaming tiles (rows 64..127
